@@ -1,0 +1,78 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check each trips a pin.
+
+Each mutation is a textual edit of the oracle's source, executed as a fresh module; the
+real oracle is untouched.  A mutation that no pin catches would mean the pins leave that
+part of the oracle unchecked.
+"""
+import importlib.util
+import os
+
+import pytest
+
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "dsv4_oracle.py")
+
+MUTATIONS = {
+    "rope_sign": [("x[..., C - r::2] = a * c - b * s", "x[..., C - r::2] = a * c + b * s"),
+                  ("x[..., C - r + 1::2] = a * s + b * c", "x[..., C - r + 1::2] = -a * s + b * c")],
+    "rope_frequency": [("np.power(float(base), -2.0 * i / r)", "np.power(float(base), -1.0 * i / r)")],
+    "rope_split_halves": [("a = x[..., C - r::2].copy()", "a = x[..., C - r:C - r // 2].copy()"),
+                          ("b = x[..., C - r + 1::2].copy()", "b = x[..., C - r // 2:].copy()"),
+                          ("x[..., C - r::2] = a * c - b * s", "x[..., C - r:C - r // 2] = a * c - b * s"),
+                          ("x[..., C - r + 1::2] = a * s + b * c", "x[..., C - r // 2:] = a * s + b * c")],
+    "csa_window_shift": [("lo = (w - 1) * m if overlap else w * m", "lo = w * m if overlap else w * m")],
+    "hca_window_shift": [("lo = (w - 1) * m if overlap else w * m", "lo = (w - 1) * m if overlap else w * m + 1")],
+    "bias_dropped": [("a += np.asarray(bias, dtype=np.float64)[slots]", "a += 0.0")],
+    "bias_slot_reversed": [("a += np.asarray(bias, dtype=np.float64)[slots]",
+                            "a += np.asarray(bias, dtype=np.float64)[::-1][slots]")],
+    "entry_rope_position": [("pos = (np.arange(entry_begin, entry_end) + 1) * m - 1 + pos_offset",
+                             "pos = np.arange(entry_begin, entry_end) * m + pos_offset")],
+    "visibility_off_by_one": [("v = (t + 1) // m", "v = t // m")],
+    "window_one_too_many": [("return range(max(0, t - window + 1), t + 1)",
+                             "return range(max(0, t - window), t + 1)")],
+    "window_excludes_self": [("return range(max(0, t - window + 1), t + 1)",
+                              "return range(max(0, t - window + 1), t)")],
+    "relu_dropped": [("(wv[:, None] * np.maximum(dots, 0.0)).sum(axis=0)", "(wv[:, None] * dots).sum(axis=0)")],
+    "head_weight_dropped": [("(wv[:, None] * np.maximum(dots, 0.0)).sum(axis=0)",
+                             "np.maximum(dots, 0.0).sum(axis=0)")],
+    "topk_tie_high_index": [("key=lambda w: (-s[w], w)", "key=lambda w: (-s[w], -w)")],
+    "topk_smallest": [("key=lambda w: (-s[w], w)", "key=lambda w: (s[w], w)")],
+    "sink_dropped": [("denom = np.exp(s - M) + e.sum(axis=1)", "denom = e.sum(axis=1)")],
+    "sink_sign": [("denom = np.exp(s - M) + e.sum(axis=1)", "denom = np.exp(-s - M) + e.sum(axis=1)")],
+    "scale_dropped": [("z = (qr @ K.T) * scale", "z = (qr @ K.T)")],
+    "no_counter_rotation": [("return rope(o, -p_t, rope_dim, base)", "return o")],
+    "counter_rotation_sign": [("return rope(o, -p_t, rope_dim, base)", "return rope(o, p_t, rope_dim, base)")],
+    "query_not_rotated": [("qr = rope(q, p_t, rope_dim, base)", "qr = q")],
+    "window_not_rotated": [("out[b] = rope(kv[b], pos, rope_dim, base)", "out[b] = kv[b]")],
+    "sentinel_not_masked": [("sel = sel[sel >= 0]", "sel = sel")],
+    "signed_zero_not_canonical": [("s = np.asarray(scores, dtype=np.float64) + 0.0",
+                                   "s = np.asarray(scores, dtype=np.float64)"),
+                                  ("key=lambda w: (-s[w], w)",
+                                   "key=lambda w: (-s[w], 0 if np.signbit(s[w]) else -1, w)")],
+}
+
+
+def _mutant(edits):
+    with open(SRC) as f:
+        text = f.read()
+    for old, new in edits:
+        assert text.count(old) == 1, f"mutation anchor not unique/absent: {old!r}"
+        text = text.replace(old, new)
+    spec = importlib.util.spec_from_loader("oracle_mutant", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(text, SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    mod = _mutant(MUTATIONS[name])
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure of a pin counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"mutation {name} passed every pin"
