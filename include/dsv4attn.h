@@ -1,0 +1,171 @@
+/*
+ * dsv4attn.h - C ABI of the MI355X (gfx950) DeepSeek-V4 hybrid attention core.
+ *
+ * The operations follow the Hugging Face Transformers model page "DeepSeek-V4":
+ *   "Hybrid attention (§2.3)"  - CSA (compressed pool at rate m with overlapping windows,
+ *                                then the Lightning Indexer's top-k), HCA (pool at rate m'
+ *                                with disjoint windows, every entry attended), and the shared
+ *                                skeleton: one K=V head, interleaved partial RoPE on the
+ *                                trailing qk_rope_head_dim channels, output rotation at
+ *                                position -i (eq. 26), per-head sink (eq. 27), and the
+ *                                sliding-window K=V branch concatenated before the pool.
+ *   "Attention mask layout"    - which keys each query sees (window cut, -1 sentinel,
+ *                                entry w visible iff w < (t+1)//m).
+ *   "DeepseekV4Config"         - field meanings (head_dim, sliding_window, index_topk ...).
+ * The page names eqs. 13-17, 26, 27 without printing them; the exact forms used here are
+ * the readings listed beside each function.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the caller owns
+ *     all buffers.  The library never allocates or frees device memory; scratch memory is
+ *     passed in explicitly (csa_index_topk's workspace).
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue work and
+ *     return; results are ready when the stream reaches them.
+ *   - Tensors are dense row-major with the channel axis innermost.  dtype DSV4_FP32 or
+ *     DSV4_BF16 applies to the activation tensors (q, kv, gate, pools, windows, outputs);
+ *     slot biases, sinks, indexer weights and scores are always float32; indices int32.
+ *   - Positions: every query / token / entry has a sequence index (its row in the
+ *     sequence); its RoPE position is that index plus rope_pos_offset.  Visibility always
+ *     uses sequence indices.  RoPE (reading R10): pair i of the trailing r channels is
+ *     (C-r+2i, C-r+2i+1), frequency rope_theta^(-2i/r), angle = position * frequency,
+ *     angles evaluated in double precision.
+ *   - Return value: DSV4_OK, or an error code.  Arguments are validated before any work is
+ *     enqueued; on error nothing is launched and dsv4_last_error() (per calling thread)
+ *     describes the problem.  DSV4_ERR_LAUNCH reports a failed kernel launch.
+ *   - Index arguments read on the device (topk_idx) are bounds-checked by the kernels:
+ *     any value outside [0, N_cap) is treated as the -1 sentinel.
+ */
+#ifndef DSV4ATTN_H
+#define DSV4ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSV4_ABI_VERSION 1
+
+enum dsv4_dtype { DSV4_FP32 = 0, DSV4_BF16 = 1 };
+
+enum dsv4_status {
+  DSV4_OK = 0,
+  DSV4_ERR_INVALID = 1,     /* null required pointer, bad or inconsistent sizes         */
+  DSV4_ERR_UNSUPPORTED = 2, /* valid request outside what the compiled kernels cover     */
+  DSV4_ERR_LAUNCH = 3,      /* the HIP runtime rejected a kernel launch                  */
+  DSV4_ERR_WORKSPACE = 4    /* workspace pointer NULL or smaller than required           */
+};
+
+int dsv4_abi_version(void);
+const char* dsv4_status_string(int status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* dsv4_last_error(void);
+
+/*
+ * csa_compress - pool tokens into compressed KV entries ("Hybrid attention (§2.3)", CSA and
+ * HCA items; "Attention mask layout", HCA paragraph for the window of an entry).
+ *
+ * Reading R1/R2/R5: for each entry w in [entry_begin, entry_end) and channel c,
+ *   window(w) = tokens [(w-1)m, (w+1)m) if overlap (CSA, 2m slots) else [w m, (w+1) m)
+ *               (HCA, m slots); slot s = token - window start; tokens before 0 are absent
+ *               and excluded from the softmax;
+ *   a_j       = gate[b,j,c] + bias[s,c]            (bias NULL: zero)
+ *   pool[b,w,c] = sum_j softmax_j(a)_j * x[b,j,c]
+ *   then channels [C-rope_dim, C) are rotated at position (w+1)m - 1 + rope_pos_offset.
+ *
+ *   x, gate : [B, S, C] dtype.   bias : [overlap ? 2m : m, C] float32 or NULL.
+ *   pool    : [B, N_cap, C] dtype; rows [entry_begin, entry_end) are written, others kept.
+ *   Requires 0 <= entry_begin <= entry_end <= N_cap, entry_end * m <= S (every window is
+ *   closed), C even and C <= 8192, rope_dim even and <= C, m >= 1.
+ */
+int csa_compress(const void* x, const void* gate, const float* bias, void* pool, int B, int S,
+                 int C, int m, int overlap, int entry_begin, int entry_end, int N_cap,
+                 int rope_dim, double rope_theta, long long rope_pos_offset, int dtype,
+                 void* stream);
+
+/*
+ * csa_index_topk - Lightning Indexer scores and top-k per query ("Hybrid attention (§2.3)",
+ * CSA item, eqs. 13-17; "Attention mask layout", CSA paragraph for the -1 sentinel;
+ * "DeepseekV4Config": index_n_heads, index_head_dim, index_topk).
+ *
+ * Query t of sequence b has sequence index q_pos0[b] + t and V = min((q_pos0[b]+t+1)//m,
+ * n_pool[b]) candidate entries (reading R7).  Reading R8:
+ *   score[w] = sum_h w_idx[b,t,h] * max(0, sum_c q_idx[b,t,h,c] * k_pool[b,w,c]),  w < V.
+ * Reading R9: the min(k, V) largest scores are kept; equal scores keep the lower entry
+ * index; -0.0 ranks as +0.0.  topk_idx[b,t,:] lists the kept entries in ascending index
+ * order, then -1 in the remaining slots; topk_score (optional) holds their scores (and 0
+ * beside each -1).
+ *
+ *   q_idx   : [B, T, nI, cI] dtype.  w_idx : [B, T, nI] float32.
+ *   k_pool  : [B, N_cap, cI] dtype (the indexer's own compressed keys, not rotated).
+ *   q_pos0, n_pool : [B] int32 device arrays.
+ *   topk_idx: [B, T, k] int32 out.  topk_score: [B, T, k] float32 out, or NULL.
+ *   workspace: device scratch of at least csa_index_topk_workspace_size(...) bytes; its
+ *   contents are overwritten.
+ *   Requires k >= 1, k <= N_cap, k <= 4096, N_cap <= 1<<20.
+ */
+size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int k);
+int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_pool, const int* q_pos0,
+                   const int* n_pool, int* topk_idx, float* topk_score, int B, int T, int nI,
+                   int cI, int N_cap, int m, int k, void* workspace, size_t workspace_bytes,
+                   int dtype, void* stream);
+
+/*
+ * swa_concat - rotate raw K=V rows into the sliding-window buffer ("Hybrid attention
+ * (§2.3)", sliding-window K=V branch and partial RoPE items).  Row i of kv_raw[b] is the
+ * token at sequence index new_pos0[b] + i; it is rotated at that index + rope_pos_offset
+ * and written to kv_win[b, new_pos0[b] + i - kv_pos0[b]] (rows outside [0, S_cap) are
+ * skipped).  The window buffer then feeds the attention calls, whose key order is
+ * [window rows || compressed entries].  kv_raw may alias kv_win when the rows coincide.
+ *
+ *   kv_raw : [B, S_new, D] dtype.  kv_win : [B, S_cap, D] dtype.
+ *   kv_pos0, new_pos0 : [B] int32 device arrays.  D even, rope_dim even and <= D.
+ */
+int swa_concat(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0, int B,
+               int S_new, int S_cap, int D, int rope_dim, double rope_theta,
+               long long rope_pos_offset, int dtype, void* stream);
+
+/*
+ * csa_attend - CSA core attention over [window || selected entries] ("Hybrid attention
+ * (§2.3)", shared skeleton; "Attention mask layout", CSA paragraph).
+ *
+ * For query t of sequence b at sequence index p = q_pos0[b] + t, the keys are the window
+ * rows for sequence indices max(0, p-window+1) .. p (reading R11; row = index - kv_pos0[b],
+ * rows outside [0, S_kv) are skipped) followed by pool rows topk_idx[b,t,i] for every
+ * valid slot i.  Key = value = that (already rotated) row (R15).  With q_rot = q rotated
+ * at p + rope_pos_offset (R10) and z_x = scale * <q_rot[h], key_x> (R12):
+ *   o[h] = sum_x e^{z_x} key_x / (e^{sink[h]} + sum_x e^{z_x})          (eq. 27, R13)
+ *   out[b,t,h] = o[h] with channels [D-rope_dim, D) rotated at -(p + rope_pos_offset)
+ *                                                                         (eq. 26, R16)
+ *   q   : [B, T, H, D] dtype, not rotated.  kv_win : [B, S_kv, D] dtype, rotated.
+ *   pool: [B, N_cap, D] dtype, rotated.  topk_idx : [B, T, k] int32.  sink : [H] float32.
+ *   kv_pos0, q_pos0 : [B] int32 device arrays.  out : [B, T, H, D] dtype.
+ *   scale <= 0 selects 1/sqrt(D).  Requires window >= 1, D even, rope_dim even <= D.
+ */
+int csa_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
+               int N_cap, const int* topk_idx, int k, const float* sink, const int* q_pos0,
+               void* out, int B, int T, int H, int D, int window, int rope_dim,
+               double rope_theta, long long rope_pos_offset, float scale, int dtype,
+               void* stream);
+
+/*
+ * hca_attend - HCA core attention over [window || every visible entry] ("Hybrid attention
+ * (§2.3)", HCA item: no indexer, every pool entry contributes; "Attention mask layout",
+ * HCA paragraph: entry w is visible to the query at sequence index p iff w < (p+1)//m_hca).
+ * Also the sliding-only layer type: pass N_cap = 0 and pool = NULL.
+ *
+ * Identical to csa_attend except that the compressed keys of query p are pool rows
+ * 0 .. min((p+1)//m_hca, n_pool[b]) - 1 (n_pool NULL: N_cap).
+ *   pool : [B, N_cap, D] dtype or NULL when N_cap == 0.  n_pool : [B] int32 or NULL.
+ */
+int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
+               int N_cap, const int* n_pool, int m_hca, const float* sink, const int* q_pos0,
+               void* out, int B, int T, int H, int D, int window, int rope_dim,
+               double rope_theta, long long rope_pos_offset, float scale, int dtype,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV4ATTN_H */

@@ -1,0 +1,135 @@
+"""MI355X (gfx950) DeepSeek-V4 hybrid attention core: CSA + HCA + sliding window.
+
+Thin Python binding over libdsv4attn.so.  Each function marshals torch device tensors into
+the pointers and sizes of the C entry point of the same name (include/dsv4attn.h) and
+raises on a non-zero status; every step of the computation runs in the HIP kernels.
+PyTorch supplies device memory and the current stream only.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _lib
+
+__all__ = ["csa_compress", "csa_index_topk", "csa_index_topk_workspace_size", "swa_concat",
+           "csa_attend", "hca_attend", "abi_version", "DSV4Error", "lib"]
+
+DSV4_FP32, DSV4_BF16 = 0, 1
+
+
+class DSV4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _lib.load()
+        self.status = status
+        super().__init__(f"{fn}: {lib.dsv4_status_string(status).decode()} "
+                         f"({lib.dsv4_last_error().decode()})")
+
+
+def lib():
+    return _lib.load()
+
+
+def abi_version() -> int:
+    return lib().dsv4_abi_version()
+
+
+def _dtype(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return DSV4_BF16
+    if t.dtype == torch.float32:
+        return DSV4_FP32
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream) if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DSV4Error(fn, status)
+
+
+def csa_compress(x, gate, bias, pool, m: int, overlap: bool, entry_begin: int = 0,
+                 entry_end: Optional[int] = None, rope_dim: int = 0, rope_theta: float = 10000.0,
+                 rope_pos_offset: int = 0, stream=None) -> None:
+    """x, gate [B,S,C]; bias [2m or m, C] fp32 or None; pool [B,N_cap,C] (rows written)."""
+    B, S, C = x.shape
+    N_cap = pool.shape[1]
+    if bias is not None and tuple(bias.shape) != ((2 * m if overlap else m), C):
+        raise ValueError(f"bias must be [{2 * m if overlap else m}, {C}], got {tuple(bias.shape)}")
+    if entry_end is None:
+        entry_end = min(S // m, N_cap)
+    _check("csa_compress", lib().csa_compress(
+        _ptr(x), _ptr(gate), _ptr(bias), _ptr(pool), B, S, C, m, int(bool(overlap)), entry_begin,
+        entry_end, N_cap, rope_dim, float(rope_theta), int(rope_pos_offset), _dtype(x),
+        _stream(stream)))
+
+
+def csa_index_topk_workspace_size(B: int, T: int, N_cap: int, k: int) -> int:
+    return int(lib().csa_index_topk_workspace_size(B, T, N_cap, k))
+
+
+def csa_index_topk(q_idx, w_idx, k_pool, q_pos0, n_pool, topk_idx, topk_score, m: int,
+                   workspace, stream=None) -> None:
+    """q_idx [B,T,nI,cI]; w_idx [B,T,nI] fp32; k_pool [B,N_cap,cI]; q_pos0/n_pool [B] int32;
+    topk_idx [B,T,k] int32 out; topk_score [B,T,k] fp32 out or None; workspace uint8 tensor."""
+    B, T, nI, cI = q_idx.shape
+    N_cap = k_pool.shape[1]
+    k = topk_idx.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("csa_index_topk", lib().csa_index_topk(
+        _ptr(q_idx), _ptr(w_idx), _ptr(k_pool), _ptr(q_pos0), _ptr(n_pool), _ptr(topk_idx),
+        _ptr(topk_score), B, T, nI, cI, N_cap, m, k, _ptr(workspace), nbytes, _dtype(q_idx),
+        _stream(stream)))
+
+
+def swa_concat(kv_raw, kv_win, kv_pos0, new_pos0, rope_dim: int, rope_theta: float,
+               rope_pos_offset: int = 0, stream=None) -> None:
+    """kv_raw [B,S_new,D] -> rotated rows of kv_win [B,S_cap,D]; kv_pos0/new_pos0 [B] int32."""
+    B, S_new, D = kv_raw.shape
+    S_cap = kv_win.shape[1]
+    _check("swa_concat", lib().swa_concat(
+        _ptr(kv_raw), _ptr(kv_win), _ptr(kv_pos0), _ptr(new_pos0), B, S_new, S_cap, D, rope_dim,
+        float(rope_theta), int(rope_pos_offset), _dtype(kv_raw), _stream(stream)))
+
+
+def csa_attend(q, kv_win, kv_pos0, pool, topk_idx, sink, q_pos0, out, window: int,
+               rope_dim: int, rope_theta: float, rope_pos_offset: int = 0, scale: float = 0.0,
+               stream=None) -> None:
+    """q [B,T,H,D]; kv_win [B,S_kv,D]; pool [B,N_cap,D]; topk_idx [B,T,k]; sink [H] fp32;
+    kv_pos0/q_pos0 [B] int32; out [B,T,H,D]."""
+    B, T, H, D = q.shape
+    _check("csa_attend", lib().csa_attend(
+        _ptr(q), _ptr(kv_win), _ptr(kv_pos0), kv_win.shape[1], _ptr(pool), pool.shape[1],
+        _ptr(topk_idx), topk_idx.shape[2], _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D,
+        window, rope_dim, float(rope_theta), int(rope_pos_offset), float(scale), _dtype(q),
+        _stream(stream)))
+
+
+def hca_attend(q, kv_win, kv_pos0, pool, n_pool, m_hca: int, sink, q_pos0, out, window: int,
+               rope_dim: int, rope_theta: float, rope_pos_offset: int = 0, scale: float = 0.0,
+               stream=None) -> None:
+    """As csa_attend, over every visible pool entry; pool None (and N_cap 0) = sliding only."""
+    B, T, H, D = q.shape
+    N_cap = 0 if pool is None else pool.shape[1]
+    _check("hca_attend", lib().hca_attend(
+        _ptr(q), _ptr(kv_win), _ptr(kv_pos0), kv_win.shape[1], _ptr(pool), N_cap, _ptr(n_pool),
+        m_hca, _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D, window, rope_dim,
+        float(rope_theta), int(rope_pos_offset), float(scale), _dtype(q), _stream(stream)))

@@ -1,0 +1,190 @@
+// Host side of the dsv4attn C ABI: argument validation, kernel dispatch, status reporting.
+// Declarations and argument meaning: include/dsv4attn.h.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/dsv4attn.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return DSV4_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSV4_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int dtype) { return dtype == DSV4_FP32 || dtype == DSV4_BF16; }
+
+#define REQUIRE(cond, ...)                                  \
+  do {                                                      \
+    if (!(cond)) return fail(DSV4_ERR_INVALID, __VA_ARGS__); \
+  } while (0)
+
+int check_rope(int rope_dim, int C, double theta) {
+  REQUIRE(rope_dim >= 0 && rope_dim % 2 == 0 && rope_dim <= C, "rope_dim %d must be even and in [0, %d]", rope_dim, C);
+  if (rope_dim > dsv4::kMaxRope) return fail(DSV4_ERR_UNSUPPORTED, "rope_dim %d above %d", rope_dim, dsv4::kMaxRope);
+  REQUIRE(rope_dim == 0 || theta > 0.0, "rope_theta must be positive");
+  return DSV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsv4_abi_version(void) { return DSV4_ABI_VERSION; }
+
+const char* dsv4_status_string(int status) {
+  switch (status) {
+    case DSV4_OK: return "ok";
+    case DSV4_ERR_INVALID: return "invalid argument";
+    case DSV4_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DSV4_ERR_LAUNCH: return "kernel launch failed";
+    case DSV4_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* dsv4_last_error(void) { return g_last_error; }
+
+int csa_compress(const void* x, const void* gate, const float* bias, void* pool, int B, int S,
+                 int C, int m, int overlap, int entry_begin, int entry_end, int N_cap,
+                 int rope_dim, double rope_theta, long long rope_pos_offset, int dtype,
+                 void* stream) {
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(B >= 0 && S >= 0 && N_cap >= 0, "negative size");
+  REQUIRE(m >= 1, "m must be >= 1");
+  REQUIRE(overlap == 0 || overlap == 1, "overlap must be 0 or 1");
+  REQUIRE(C >= 2 && C % 2 == 0, "C must be even and >= 2");
+  if (!(C % 8 == 0 ? C <= 2048 : C <= 512))
+    return fail(DSV4_ERR_UNSUPPORTED, "C=%d: need C <= 2048 (multiple of 8) or <= 512", C);
+  REQUIRE(0 <= entry_begin && entry_begin <= entry_end && entry_end <= N_cap,
+          "entries [%d,%d) outside [0,N_cap=%d]", entry_begin, entry_end, N_cap);
+  REQUIRE(static_cast<long long>(entry_end) * m <= S, "entry %d's window is not closed by S=%d", entry_end - 1, S);
+  if (int rc = check_rope(rope_dim, C, rope_theta)) return rc;
+  if (B == 0 || entry_begin == entry_end) return ok();
+  REQUIRE(x && gate && pool, "null x/gate/pool");
+  REQUIRE(aligned16(x) && aligned16(gate) && aligned16(pool) && (!bias || aligned16(bias)),
+          "pointers must be 16-byte aligned");
+  return launched(dsv4::launch_compress(x, gate, bias, pool, B, S, C, m, overlap, entry_begin,
+                                        entry_end, N_cap, rope_dim, rope_theta, rope_pos_offset,
+                                        dtype, static_cast<hipStream_t>(stream)),
+                  "csa_compress");
+}
+
+size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int k) {
+  (void)k;
+  if (B <= 0 || T <= 0 || N_cap <= 0) return 0;
+  return static_cast<size_t>(B) * T * N_cap * sizeof(float);
+}
+
+int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_pool, const int* q_pos0,
+                   const int* n_pool, int* topk_idx, float* topk_score, int B, int T, int nI,
+                   int cI, int N_cap, int m, int k, void* workspace, size_t workspace_bytes,
+                   int dtype, void* stream) {
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(B >= 0 && T >= 0, "negative size");
+  REQUIRE(nI >= 1 && cI >= 1, "nI, cI must be >= 1");
+  REQUIRE(m >= 1, "m must be >= 1");
+  REQUIRE(N_cap >= 1 && N_cap <= (1 << 20), "N_cap %d outside [1, 2^20]", N_cap);
+  REQUIRE(k >= 1 && k <= N_cap, "k %d outside [1, N_cap=%d]", k, N_cap);
+  if (k > 4096) return fail(DSV4_ERR_UNSUPPORTED, "k %d above 4096", k);
+  if (!dsv4::index_scores_fast(nI, cI, dtype) && nI * cI + nI > 16384)
+    return fail(DSV4_ERR_UNSUPPORTED, "nI*cI=%d too large for the generic indexer", nI * cI);
+  if (B == 0 || T == 0) return ok();
+  REQUIRE(q_idx && w_idx && k_pool && q_pos0 && n_pool && topk_idx, "null required pointer");
+  REQUIRE(aligned16(q_idx) && aligned16(k_pool) && aligned16(w_idx), "pointers must be 16-byte aligned");
+  const size_t need = csa_index_topk_workspace_size(B, T, N_cap, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSV4_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  float* scores = static_cast<float*>(workspace);
+  hipError_t e = dsv4::launch_index_scores(q_idx, w_idx, k_pool, q_pos0, n_pool, scores, B, T, nI,
+                                           cI, N_cap, m, dtype, st);
+  if (e != hipSuccess) return launched(e, "csa_index_topk (scores)");
+  return launched(dsv4::launch_topk(scores, q_pos0, n_pool, topk_idx, topk_score, B, T, N_cap, m,
+                                    k, st),
+                  "csa_index_topk (select)");
+}
+
+int swa_concat(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0, int B,
+               int S_new, int S_cap, int D, int rope_dim, double rope_theta,
+               long long rope_pos_offset, int dtype, void* stream) {
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(B >= 0 && S_new >= 0 && S_cap >= 0, "negative size");
+  REQUIRE(D >= 2 && D % 2 == 0, "D must be even and >= 2");
+  if (int rc = check_rope(rope_dim, D, rope_theta)) return rc;
+  if (B == 0 || S_new == 0 || S_cap == 0) return ok();
+  REQUIRE(kv_raw && kv_win && kv_pos0 && new_pos0, "null required pointer");
+  REQUIRE(aligned16(kv_raw) && aligned16(kv_win), "pointers must be 16-byte aligned");
+  return launched(dsv4::launch_swa(kv_raw, kv_win, kv_pos0, new_pos0, B, S_new, S_cap, D, rope_dim,
+                                   rope_theta, rope_pos_offset, dtype,
+                                   static_cast<hipStream_t>(stream)),
+                  "swa_concat");
+}
+
+static int attend_common(dsv4::AttendArgs& a, void* stream, const char* name) {
+  REQUIRE(dtype_ok(a.dtype), "dtype %d", a.dtype);
+  REQUIRE(a.B >= 0 && a.T >= 0 && a.S_kv >= 0 && a.N_cap >= 0, "negative size");
+  REQUIRE(a.H >= 1 && a.D >= 2 && a.D % 2 == 0, "H >= 1 and even D >= 2 required");
+  REQUIRE(a.window >= 1, "window must be >= 1");
+  if (int rc = check_rope(a.r, a.D, a.theta)) return rc;
+  if (a.scale <= 0.f) a.scale = 1.0f / sqrtf(static_cast<float>(a.D));
+  if (a.B == 0 || a.T == 0) return ok();
+  REQUIRE(a.q && a.kv_win && a.kv_pos0 && a.sink && a.q_pos0 && a.out, "null required pointer");
+  REQUIRE(a.N_cap == 0 || a.pool, "pool required when N_cap > 0");
+  REQUIRE(aligned16(a.q) && aligned16(a.kv_win) && aligned16(a.out) && (!a.pool || aligned16(a.pool)),
+          "pointers must be 16-byte aligned");
+  if (!dsv4::attend_fast(a.H, a.D, a.r, a.dtype)) {
+    if (a.D > 4096) return fail(DSV4_ERR_UNSUPPORTED, "D=%d above 4096 for the generic kernel", a.D);
+    const long long max_keys = static_cast<long long>(a.window) + (a.csa ? a.k : a.N_cap);
+    if (max_keys > dsv4::attend_generic_max_keys())
+      return fail(DSV4_ERR_UNSUPPORTED, "%lld keys per query exceed the generic kernel's %d", max_keys,
+                  dsv4::attend_generic_max_keys());
+  }
+  return launched(dsv4::launch_attend(a, static_cast<hipStream_t>(stream)), name);
+}
+
+int csa_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
+               int N_cap, const int* topk_idx, int k, const float* sink, const int* q_pos0,
+               void* out, int B, int T, int H, int D, int window, int rope_dim,
+               double rope_theta, long long rope_pos_offset, float scale, int dtype,
+               void* stream) {
+  REQUIRE(k >= 1, "k must be >= 1");
+  if (k > 4096) return fail(DSV4_ERR_UNSUPPORTED, "k %d above 4096", k);
+  REQUIRE(B == 0 || T == 0 || topk_idx, "null topk_idx");
+  dsv4::AttendArgs a{q, kv_win, kv_pos0, S_kv, pool, N_cap, topk_idx, k, nullptr, 1, sink, q_pos0,
+                     out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, true};
+  return attend_common(a, stream, "csa_attend");
+}
+
+int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
+               int N_cap, const int* n_pool, int m_hca, const float* sink, const int* q_pos0,
+               void* out, int B, int T, int H, int D, int window, int rope_dim,
+               double rope_theta, long long rope_pos_offset, float scale, int dtype,
+               void* stream) {
+  REQUIRE(m_hca >= 1, "m_hca must be >= 1");
+  dsv4::AttendArgs a{q, kv_win, kv_pos0, S_kv, pool, N_cap, nullptr, 0, n_pool, m_hca, sink, q_pos0,
+                     out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, false};
+  return attend_common(a, stream, "hca_attend");
+}
+
+}  // extern "C"

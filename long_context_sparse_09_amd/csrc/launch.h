@@ -1,0 +1,56 @@
+// Internal kernel launchers of the dsv4attn library (host side, called after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace dsv4 {
+
+hipError_t launch_compress(const void* x, const void* gate, const float* bias, void* pool, int B,
+                           int S, int C, int m, int overlap, int e0, int e1, int N_cap, int r,
+                           double theta, long long off, int dtype, hipStream_t st);
+
+hipError_t launch_swa(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0,
+                      int B, int S_new, int S_cap, int D, int r, double theta, long long off,
+                      int dtype, hipStream_t st);
+
+// Scores of every visible (query, entry) pair into scores[B*T][N_cap] (fp32).
+hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void* k_pool,
+                               const int* q_pos0, const int* n_pool, float* scores, int B, int T,
+                               int nI, int cI, int N_cap, int m, int dtype, hipStream_t st);
+
+// Top-k selection from scores[B*T][N_cap].
+hipError_t launch_topk(const float* scores, const int* q_pos0, const int* n_pool, int* topk_idx,
+                       float* topk_score, int B, int T, int N_cap, int m, int k, hipStream_t st);
+
+struct AttendArgs {
+  const void* q;
+  const void* kv_win;
+  const int* kv_pos0;
+  int S_kv;
+  const void* pool;
+  int N_cap;
+  const int* topk_idx;  // CSA: [B,T,k]; HCA: NULL
+  int k;
+  const int* n_pool;  // HCA: [B] or NULL
+  int m_hca;
+  const float* sink;
+  const int* q_pos0;
+  void* out;
+  int B, T, H, D, window, r;
+  double theta;
+  long long pos_off;
+  float scale;
+  int dtype;
+  bool csa;
+};
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+// Whether the MFMA fast paths cover a shape (otherwise the generic kernels run).
+bool index_scores_fast(int nI, int cI, int dtype);
+bool attend_fast(int H, int D, int r, int dtype);
+// Keys one query may see at most (sizes the generic attention kernel's LDS).
+int attend_generic_max_keys();
+
+}  // namespace dsv4

@@ -290,10 +290,13 @@ def csa_index_topk(q_idx, w_idx, k_pool, q_pos0, n_pool, m, k, rows=None):
 
 
 def _window_keys(kv_win_b, kv_pos0_b, qpos, window):
+    """Window rows of the query at sequence index qpos held by a buffer whose row 0 is
+    sequence index kv_pos0_b.  Rows the buffer does not hold are skipped (the library's
+    documented boundary rule for a window buffer that starts late or ends early)."""
     lo = max(0, qpos - window + 1)
-    r0, r1 = lo - kv_pos0_b, qpos + 1 - kv_pos0_b
-    assert 0 <= r0 <= r1 <= kv_win_b.shape[0], "window rows outside the window buffer"
-    return kv_win_b[r0:r1]
+    r0 = max(lo - kv_pos0_b, 0)
+    r1 = min(qpos + 1 - kv_pos0_b, kv_win_b.shape[0])
+    return kv_win_b[r0:max(r0, r1)]
 
 
 def csa_attend(q, kv_win, kv_pos0, pool, topk_idx, sink, q_pos0, window, rope_dim, base,

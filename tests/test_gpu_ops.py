@@ -1,0 +1,255 @@
+"""Per-call GPU parity: each C-ABI entry point against the CPU oracle on the same inputs.
+
+Inputs come from the seeded workload generator (keyed by test name); the oracle receives the
+exact fp64 values of the stored inputs.  Tolerances: fp32 |d| <= 1e-5 max|ref|; bf16
+|d| <= 2e-2 max|ref| (and pool / window rows within one bf16 ulp of the exact value); top-k
+sets exact except within the 1e-4 relative band around the k-th score.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import (assert_bf16_ulp, assert_close, check_topk_row, dev, enc, host,
+                      torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU machines only to be skipped
+    pytest.skip("no GPU", allow_module_level=True)
+
+import long_context_sparse_09_amd as L  # noqa: E402
+
+
+def normal(name, shape, seed=101):
+    return W.normal_tensor(seed, 0, name, shape).astype(np.float64)
+
+
+def i32(v):
+    return torch.tensor(np.asarray(v, dtype=np.int32), device="cuda")
+
+
+# ---------------------------------------------------------------------------- compress
+
+COMPRESS_CASES = [
+    # dtype, B, S, C, m, overlap, rope, bias, entries
+    ("fp32", 1, 259, 64, 4, True, 16, True, None),     # tiny-CSA shape, ragged tail
+    ("fp32", 1, 256, 32, 4, True, 0, True, None),      # tiny indexer keys
+    ("fp32", 2, 37, 6, 2, True, 2, True, None),        # C not a multiple of 8
+    ("bf16", 1, 1030, 512, 4, True, 64, True, None),   # CSA K=V pool
+    ("bf16", 2, 1030, 128, 4, True, 0, True, None),    # indexer keys, B = 2
+    ("bf16", 1, 1000, 512, 128, False, 64, True, None),  # HCA, 7 entries + tail
+    ("bf16", 1, 700, 512, 128, False, 64, False, None),  # HCA, no bias
+    ("bf16", 1, 300, 512, 4, True, 64, True, (20, 41)),  # entry sub-range (chunked prefill)
+    ("bf16", 1, 90, 96, 3, True, 8, False, None),      # odd rate
+]
+
+
+@pytest.mark.parametrize("case", COMPRESS_CASES, ids=lambda c: "-".join(map(str, c[:7])))
+def test_csa_compress(case):
+    dt, B, S, C, m, overlap, r, use_bias, entries = case
+    x = normal("x", (B, S, C))
+    g = normal("g", (B, S, C))
+    span = 2 * m if overlap else m
+    bias = normal("bias", (span, C)).astype(np.float32) if use_bias else None
+    xs, gs = enc(x, dt), enc(g, dt)
+    x64, g64 = W.to_f64(xs), W.to_f64(gs)
+    N = S // m
+    e0, e1 = entries if entries else (0, N)
+    base, off = 10000.0, 37
+    pool = torch.full((B, N, C), 7.0, dtype=torch_dtype(dt), device="cuda")
+    L.csa_compress(dev(xs), dev(gs), None if bias is None else dev(bias), pool, m, overlap, e0, e1,
+                   r, base, off)
+    got = host(pool)
+    ref = oracle.csa_compress(x64, g64, None if bias is None else bias.astype(np.float64), m,
+                              overlap, r, base, off, e0, e1)
+    assert np.all(got[:, :e0] == 7.0) and np.all(got[:, e1:] == 7.0), "rows outside the range"
+    assert_close(got[:, e0:e1], ref, dt, "pool")
+    if dt == "bf16":
+        assert_bf16_ulp(got[:, e0:e1], ref, "pool")
+
+
+# ---------------------------------------------------------------------------- swa_concat
+
+@pytest.mark.parametrize("dt,D,r", [("fp32", 64, 16), ("bf16", 512, 64), ("bf16", 512, 0)])
+def test_swa_concat(dt, D, r):
+    B, S_new, S_cap = 2, 300, 400
+    kv = normal("kv", (B, S_new, D))
+    kvs = enc(kv, dt)
+    kv_pos0, new_pos0, off = [0, 50], [0, 60], 12345
+    win = torch.full((B, S_cap, D), 3.0, dtype=torch_dtype(dt), device="cuda")
+    L.swa_concat(dev(kvs), win, i32(kv_pos0), i32(new_pos0), r, 10000.0, off)
+    got = host(win)
+    ref = oracle.swa_concat(W.to_f64(kvs), new_pos0, r, 10000.0, off)
+    for b in range(B):
+        r0 = new_pos0[b] - kv_pos0[b]
+        assert np.all(got[b, :r0] == 3.0) and np.all(got[b, r0 + S_new:] == 3.0)
+        assert_close(got[b, r0:r0 + S_new], ref[b], dt, f"window b={b}")
+        if dt == "bf16":
+            assert_bf16_ulp(got[b, r0:r0 + S_new], ref[b], "window")
+
+
+def test_swa_concat_in_place_and_clipped():
+    B, S, D, r = 1, 64, 512, 64
+    kvs = enc(normal("kv", (B, S, D)), "bf16")
+    t = dev(kvs)
+    L.swa_concat(t, t, i32([0]), i32([0]), r, 10000.0, 0)  # in place
+    assert_close(host(t), oracle.swa_concat(W.to_f64(kvs), [0], r, 10000.0), "bf16", "in place")
+    # rows landing outside [0, S_cap) are skipped
+    win = torch.zeros(B, 16, D, dtype=torch.bfloat16, device="cuda")
+    L.swa_concat(dev(kvs), win, i32([40]), i32([30]), r, 10000.0, 0)
+    ref = oracle.swa_concat(W.to_f64(kvs), [30], r, 10000.0)
+    assert_close(host(win)[0], ref[0, 10:26], "bf16", "clipped rows")
+
+
+# ---------------------------------------------------------------------------- index + top-k
+
+def _topk_case(dt, B, T, nI, cI, N_cap, k, m, q_pos0, n_pool, seed, ties=False):
+    q = normal("q_idx", (B, T, nI, cI), seed)
+    w = normal("w_idx", (B, T, nI), seed).astype(np.float32)
+    kp = normal("k_pool", (B, N_cap, cI), seed)
+    if ties:
+        # positive queries and weights; entries >= 10 are all -1, so their score is exactly 0:
+        # the k-th slot falls inside a block of exact zero ties (lowest indices must win);
+        # entry 5 duplicates entry 3 (an exact tie among positive scores)
+        q, w = np.abs(q), np.abs(w)
+        kp[:, 10:] = -1.0
+        kp[:, 5] = kp[:, 3]
+    qs, ks = enc(q, dt), enc(kp, dt)
+    k_eff = k
+    idx = torch.empty(B, T, k_eff, dtype=torch.int32, device="cuda")
+    sc = torch.empty(B, T, k_eff, dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.csa_index_topk_workspace_size(B, T, N_cap, k_eff), dtype=torch.uint8,
+                     device="cuda")
+    L.csa_index_topk(dev(qs), dev(w), dev(ks), i32(q_pos0), i32(n_pool), idx, sc, m, ws)
+    gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
+    q64, k64 = W.to_f64(qs), W.to_f64(ks)
+    swaps = 0
+    for b in range(B):
+        for t in range(T):
+            V = oracle.n_visible(q_pos0[b] + t, m, min(n_pool[b], N_cap))
+            s = oracle.index_scores(q64[b, t], w[b, t], k64[b, :V])
+            swaps += check_topk_row(gi[b, t], s, k_eff, f"b={b} t={t}")
+            valid = gi[b, t] >= 0
+            if valid.any():
+                ref = s[gi[b, t][valid]]
+                assert np.allclose(gs[b, t][valid], ref, rtol=1e-4, atol=1e-4 * np.abs(s).max())
+            assert np.all(gs[b, t][~valid] == 0.0)
+    return swaps
+
+
+def test_index_topk_tiny_fp32():
+    w = W.workload(1)
+    _topk_case("fp32", 1, w.S, w.nI, w.cI, w.S // w.m, w.k, w.m, [0], [w.S // w.m], 5)
+
+
+def test_index_topk_prefill_bf16_mfma():
+    # 64 heads x 128 (MFMA path), T not a multiple of the 8-query block, k > some V(t)
+    _topk_case("bf16", 1, 1003, 64, 128, 250, 100, 4, [0], [250], 6)
+
+
+def test_index_topk_prefill_offset_batches():
+    # two sequences with different start positions and pool fill levels
+    _topk_case("bf16", 2, 72, 64, 128, 700, 64, 4, [2000, 5], [650, 700], 7)
+
+
+def test_index_topk_decode_split():
+    # T = 1 per sequence: the split-N decode path; n_pool caps visibility
+    _topk_case("bf16", 3, 1, 64, 128, 2300, 512, 4, [4000, 9000, 200], [1000, 2250, 50], 8)
+
+
+def test_index_topk_exact_ties():
+    _topk_case("bf16", 1, 40, 64, 128, 60, 16, 4, [300], [60], 9, ties=True)
+    _topk_case("fp32", 1, 40, 4, 32, 60, 16, 4, [300], [60], 10, ties=True)
+
+
+# ---------------------------------------------------------------------------- attention
+
+def _attend_case(dt, csa, B, T, H, D, r, Wn, S_kv, kv_pos0, q_pos0, N_cap, k=0, n_pool=None,
+                 m_hca=16, seed=20, shuffle_invalid=False):
+    q = normal("q", (B, T, H, D), seed)
+    win = normal("win", (B, S_kv, D), seed)
+    pool = normal("pool", (B, max(N_cap, 1), D), seed)[:, :N_cap]
+    sink = normal("sink", (H,), seed).astype(np.float32)
+    qs, ws_, ps = enc(q, dt), enc(win, dt), enc(pool, dt)
+    base, off = 10000.0, 11
+    out = torch.empty(B, T, H, D, dtype=torch_dtype(dt), device="cuda")
+    pool_t = dev(ps) if N_cap > 0 else None
+    if csa:
+        topk = W.random_index_lists(seed, "topk", B, T, k, N_cap, shuffle_invalid)
+        L.csa_attend(dev(qs), dev(ws_), i32(kv_pos0), pool_t, dev(topk), dev(sink), i32(q_pos0),
+                     out, Wn, r, base, off)
+        ref = oracle.csa_attend(W.to_f64(qs), W.to_f64(ws_), kv_pos0, W.to_f64(ps), topk, sink,
+                                q_pos0, Wn, r, base, off)
+    else:
+        L.hca_attend(dev(qs), dev(ws_), i32(kv_pos0), pool_t,
+                     i32(n_pool) if n_pool is not None else None, m_hca, dev(sink), i32(q_pos0),
+                     out, Wn, r, base, off)
+        ref = oracle.hca_attend(W.to_f64(qs), W.to_f64(ws_), kv_pos0,
+                                W.to_f64(ps) if N_cap > 0 else None,
+                                n_pool if n_pool is not None else ([N_cap] * B if N_cap else None),
+                                m_hca, sink, q_pos0, Wn, r, base, off)
+    return assert_close(host(out), ref, dt, "attention output")
+
+
+def test_csa_attend_mfma():
+    # 64 x 512 MFMA path; window + up to 96 selected keys (ragged tile counts), two sequences
+    _attend_case("bf16", True, 2, 37, 64, 512, 64, 128, 300, [0, 40], [150, 100], 300, k=96)
+
+
+def test_csa_attend_mfma_unordered_sentinels():
+    # -1 slots anywhere in the list are masked, valid slots anywhere are used
+    _attend_case("bf16", True, 1, 20, 64, 512, 64, 128, 200, [0], [180], 200, k=64, seed=21,
+                 shuffle_invalid=True)
+
+
+def test_csa_attend_generic_fp32():
+    _attend_case("fp32", True, 2, 30, 8, 64, 16, 32, 100, [0, 5], [60, 40], 64, k=16, seed=22)
+
+
+def test_hca_attend_mfma():
+    _attend_case("bf16", False, 2, 33, 64, 512, 64, 128, 400, [0, 0], [300, 7], 40,
+                 n_pool=[25, 40], m_hca=8, seed=23)
+
+
+def test_sliding_attend_mfma_window_edges():
+    # no pool; queries at the start of the sequence (fewer than W keys) and W > S
+    _attend_case("bf16", False, 1, 40, 64, 512, 64, 128, 40, [0], [0], 0, seed=24)
+    _attend_case("bf16", False, 1, 40, 64, 512, 64, 1000, 40, [0], [0], 0, seed=25)
+
+
+def test_attend_rope_zero_and_generic_bf16():
+    _attend_case("bf16", False, 1, 16, 64, 512, 0, 128, 60, [0], [40], 10, n_pool=[10], m_hca=4,
+                 seed=26)
+    _attend_case("bf16", True, 1, 16, 16, 128, 32, 20, 60, [0], [40], 30, k=8, seed=27)
+
+
+def test_decode_shaped_attend():
+    # one query per sequence at the end of its window buffer (decode layout)
+    B, Wn = 4, 128
+    L_b = [5000, 70000, 129, 20000]
+    _attend_case("bf16", True, B, 1, 64, 512, 64, Wn, Wn, [x - Wn for x in L_b],
+                 [x - 1 for x in L_b], 500, k=512, seed=28)
+
+
+# ---------------------------------------------------------------------------- errors
+
+def test_argument_errors_do_not_launch():
+    x = torch.zeros(1, 16, 64, dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros(1, 4, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(L.DSV4Error) as e:
+        L.csa_compress(x, x, None, pool, 4, True, 0, 5)  # entry 4 needs tokens up to 19
+    assert e.value.status == 1
+    with pytest.raises(L.DSV4Error) as e:
+        L.csa_compress(x, x, None, pool, 4, True, rope_dim=3)
+    assert e.value.status == 1
+    q = torch.zeros(1, 2, 4, 8, dtype=torch.float32, device="cuda")
+    kp = torch.zeros(1, 10, 8, dtype=torch.float32, device="cuda")
+    idx = torch.zeros(1, 2, 4, dtype=torch.int32, device="cuda")
+    w = torch.zeros(1, 2, 4, dtype=torch.float32, device="cuda")
+    z = i32([0])
+    small = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(L.DSV4Error) as e:
+        L.csa_index_topk(q, w, kp, z, i32([10]), idx, None, 4, small)
+    assert e.value.status == 4

@@ -23,6 +23,7 @@ Generation recipe
 from __future__ import annotations
 
 import dataclasses
+import os
 import zlib
 from typing import Dict, Iterable, Optional, Sequence
 
@@ -35,14 +36,30 @@ ROW_BLOCK = 64
 # ----------------------------------------------------------------------------
 
 
-def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 (ties to even); return uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+def _bf16_rne(u: np.ndarray) -> np.ndarray:
     nan = (u & 0x7FFFFFFF) > 0x7F800000
     rounding = ((u >> 16) & 1) + 0x7FFF
     out = ((u + rounding) >> 16).astype(np.uint16)
     out[nan] = 0x7FC0
     return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    flat = u.reshape(-1)
+    if flat.size < (1 << 24):
+        return _bf16_rne(flat).reshape(u.shape)
+    out = np.empty(flat.size, dtype=np.uint16)
+    step = 1 << 22
+    import concurrent.futures as cf
+
+    def conv(i):
+        out[i:i + step] = _bf16_rne(flat[i:i + step])
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(conv, range(0, flat.size, step)))
+    return out.reshape(u.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -143,11 +160,28 @@ def normal_rows(seed: int, layer: int, name: str, row_shape: Sequence[int],
     if len(idx) == 0:
         return out.reshape((0,) + row_shape)
     blocks = idx // ROW_BLOCK
-    for b in np.unique(blocks):
+    contiguous = bool(np.all(np.diff(idx) == 1))
+
+    def fill(b):
         gen = _block_gen(seed, layer, name, int(b))
+        b0 = int(b) * ROW_BLOCK
+        if contiguous and idx[0] <= b0 and b0 + ROW_BLOCK <= idx[-1] + 1:
+            # whole block lands contiguously in the output: draw in place
+            gen.standard_normal(out=out[b0 - idx[0]:b0 - idx[0] + ROW_BLOCK], dtype=np.float32)
+            return
         blk = gen.standard_normal(size=(ROW_BLOCK, per_row), dtype=np.float32)
         sel = np.nonzero(blocks == b)[0]
-        out[sel] = blk[idx[sel] - b * ROW_BLOCK]
+        out[sel] = blk[idx[sel] - b0]
+
+    ub = np.unique(blocks)
+    if len(ub) * ROW_BLOCK * per_row >= (1 << 22):  # large draws: blocks in parallel (fills release the GIL)
+        import concurrent.futures as cf
+
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, ub))
+    else:
+        for b in ub:
+            fill(b)
     return out.reshape((len(idx),) + row_shape)
 
 
@@ -289,3 +323,19 @@ def decode_inputs(w: Workload, n_seq: Optional[int] = None, pool_rows: Optional[
         w_idx[i] = normal_rows(w.seed, 0, "w_idx" + tag, (w.nI,), slice(0, 1), 1)
     return {"lengths": L, "pool": pool, "k_pool": k_pool, "window": window, "kv_new": kv_new,
             "q": q, "q_idx": q_idx, "w_idx": w_idx, "sink": param(w, 0, "sink")}
+
+
+def random_index_lists(seed: int, name: str, B: int, T: int, k: int, N: int,
+                       shuffle: bool = False) -> np.ndarray:
+    """int32 [B, T, k] lists of distinct entries < N, a random number (0..min(k, N)) per row,
+    padded with -1 (after the valid entries, or scattered among them when shuffle=True).
+    Synthetic inputs for the attention call, which takes index lists as given."""
+    gen = _block_gen(seed, 0, name, 0)
+    out = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = int(gen.integers(0, min(k, N) + 1))
+            out[b, t, :n] = gen.choice(N, size=n, replace=False)
+            if shuffle:
+                gen.shuffle(out[b, t])
+    return out
