@@ -42,6 +42,7 @@ constexpr int APITCH = AD * 2 + 16;          // LDS bytes per key row (16 B pad)
 constexpr int ATILE = ANK * APITCH;          // bytes per tile buffer
 constexpr int ATILES_BYTES = 2 * ATILE;      // double buffer
 constexpr int AXCH_BYTES = 2 * 2 * 2 * 64 * 16 + 2 * 2 * 64 * 4 * 2;  // P fragments, max, sum
+constexpr float kLazy = 8.f;  // log2-domain headroom before the running max moves
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
@@ -64,7 +65,7 @@ attend_mfma_kernel(AttendArgs a) {
   float* xmax = reinterpret_cast<float*>(lds + ATILES_BYTES + 2 * 2 * 2 * 64 * 16);  // [hb][kh][lane]
   float* xsum = xmax + 2 * 2 * 64;                                    // [hb][kh][lane]
   int* klist = reinterpret_cast<int*>(lds + ATILES_BYTES + AXCH_BYTES);  // CSA: selected rows
-  __shared__ double inv_freq[kMaxRope / 2];
+  __shared__ float rope_c[kMaxRope / 2], rope_s[kMaxRope / 2];  // at the query's position
   __shared__ int wave_tot[4];
 
   const int tid = threadIdx.x;
@@ -76,7 +77,14 @@ attend_mfma_kernel(AttendArgs a) {
   const int qid = gridDim.x - 1 - blockIdx.x;
   const int b = qid / a.T, t = qid % a.T;
   const long long p = static_cast<long long>(a.q_pos0[b]) + t;
-  rope_table(inv_freq, a.r, a.theta);
+  const double qpos = static_cast<double>(p + a.pos_off);
+  if (tid < a.r / 2) {  // one (cos, sin) per rotary pair, formed in double precision
+    const double inv_freq = pow(a.theta, -2.0 * tid / a.r);
+    double sn, cs;
+    sincos(qpos * inv_freq, &sn, &cs);
+    rope_c[tid] = static_cast<float>(cs);
+    rope_s[tid] = static_cast<float>(sn);
+  }
 
   // ---- key set: window rows [r0, r1) of kv_win, then compressed entries ----
   const long long lo = max(0LL, p - a.window + 1);
@@ -103,7 +111,7 @@ attend_mfma_kernel(AttendArgs a) {
     v = min(v, static_cast<long long>(a.N_cap));
     n_cmp = static_cast<int>(max(v, 0LL));
   }
-  __syncthreads();  // klist, inv_freq
+  __syncthreads();  // klist, rope table
   const int n_keys = n_win + n_cmp;
   const int n_tiles = (n_keys + ANK - 1) / ANK;
 
@@ -130,7 +138,7 @@ attend_mfma_kernel(AttendArgs a) {
   if (n_tiles > 0) issue_tile(0, 0);
 
   // ---- rotated Q^T fragments (B operand): head hb*32 + l32, dims ks*16 + half*8 .. +8 ----
-  const double qpos = static_cast<double>(p + a.pos_off);
+  const int rope0 = AD - a.r;  // first rotary channel
   bf16x8_t qf[AD / 16];
   {
     const bf16_t* qrow = static_cast<const bf16_t*>(a.q) +
@@ -138,10 +146,18 @@ attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
     for (int ks = 0; ks < AD / 16; ++ks) {
       const int c0 = ks * 16 + half * 8;
-      if (a.r > 0 && c0 + 8 > AD - a.r) {
+      if (c0 + 8 > rope0) {
         float v[8];
         Chunk<bf16_t>::load<8>(qrow + ks * 16, v);
-        rope_chunk<8>(v, c0, AD, a.r, qpos, inv_freq);
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          if (c0 + i >= rope0) {
+            const int pr = (c0 + i - rope0) >> 1;
+            const float c = rope_c[pr], sn = rope_s[pr], x = v[i], y = v[i + 1];
+            v[i] = x * c - y * sn;
+            v[i + 1] = x * sn + y * c;
+          }
+        }
         qf[ks] = pack8(v);
       } else {
         qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16));
@@ -151,7 +167,10 @@ attend_mfma_kernel(AttendArgs a) {
 
   const float c2 = a.scale * kLog2e;  // logits in the log2 domain
   const int head = hb * 32 + l32;
-  float m_run = a.sink[head] * kLog2e;  // the sink: logit s_h with value 0
+  // running reference max and softmax sum of this wave; both waves of a head block form the
+  // full denominator for their own output channels, so both start from the sink (logit s_h,
+  // value 0): max = s_h, sum = 1
+  float m_run = a.sink[head] * kLog2e;
   float l_run = 1.f;
   constexpr int NDT = AD / 2 / 32;  // output channel tiles owned by this wave
   f32x16_t o[NDT];
@@ -172,18 +191,27 @@ attend_mfma_kernel(AttendArgs a) {
     if (it + 1 < n_tiles) issue_tile(it + 1, (it + 1) & 1);
     const unsigned char* tb = tiles + (it & 1) * ATILE;
 
-    // S^T (32 keys of half kh x 32 heads) over the 512 channels
+    // S^T (32 keys of half kh x 32 heads) over the 512 channels; K fragments run 4 ahead
     f32x16_t s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
     const unsigned char* arow = tb + (kh * 32 + l32) * APITCH + half * 16;
+    {
+      constexpr int PF = 4;
+      bf16x8_t kr[PF];
 #pragma unroll
-    for (int ks = 0; ks < AD / 16; ++ks) {
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(arow + ks * 32);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+      for (int i = 0; i < PF; ++i) kr[i] = *reinterpret_cast<const bf16x8_t*>(arow + i * 32);
+#pragma unroll
+      for (int ks = 0; ks < AD / 16; ++ks) {
+        const bf16x8_t kf = kr[ks % PF];
+        if (ks + PF < AD / 16) kr[ks % PF] = *reinterpret_cast<const bf16x8_t*>(arow + (ks + PF) * 32);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+      }
     }
 
-    // tile max over both key halves (lane: head l32, keys (e/4)*8 + half*4 + e%4)
+    // online softmax over this wave's 32 keys (lane: head l32, keys (e/4)*8 + half*4 + e%4).
+    // Each wave keeps its own reference max m_run and moves it only when a logit exceeds it
+    // by more than 2^kLazy, so most tiles need no rescale of the accumulators.
     const int kbase = it * ANK + kh * 32 + half * 4;
     float tmax = -INFINITY;
 #pragma unroll
@@ -194,9 +222,7 @@ attend_mfma_kernel(AttendArgs a) {
       tmax = fmaxf(tmax, v);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    xmax[xme] = tmax;
-    __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(tmax, xmax[xpa]));  // finite: m_run >= sink
+    const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
     const float alpha = exp2f(m_run - m_new);
     float psum = 0.f;
     bf16x8_t pb[2];
@@ -208,6 +234,7 @@ attend_mfma_kernel(AttendArgs a) {
     }
     psum += __shfl_xor(psum, 32);
     xsum[xme] = psum;
+    xmax[xme] = m_new;
     xp[(hb * 2 + kh) * 128 + lane] = pb[0];
     xp[(hb * 2 + kh) * 128 + 64 + lane] = pb[1];
     if (__ballot(m_new != m_run)) {
@@ -217,11 +244,20 @@ attend_mfma_kernel(AttendArgs a) {
         for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
     }
     m_run = m_new;
-    __syncthreads();
-    l_run = l_run * alpha + psum + xsum[xpa];
+    __syncthreads();  // partner's P fragments, sum and reference max are in LDS
+    // partner's P was formed against its own reference max: bring it to this wave's
+    const float f = exp2f(xmax[xpa] - m_run);
+    l_run = l_run * alpha + psum + xsum[xpa] * f;
+    bf16x8_t px0 = xp[(hb * 2 + (kh ^ 1)) * 128 + lane];
+    bf16x8_t px1 = xp[(hb * 2 + (kh ^ 1)) * 128 + 64 + lane];
+    if (__ballot(f != 1.f)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        px0[e] = static_cast<__bf16>(static_cast<float>(px0[e]) * f);
+        px1[e] = static_cast<__bf16>(static_cast<float>(px1[e]) * f);
+      }
+    }
     // B operands for k-steps 0..3 = keys 0..63 of the tile (half kh is this wave's own)
-    const bf16x8_t px0 = xp[(hb * 2 + (kh ^ 1)) * 128 + lane];
-    const bf16x8_t px1 = xp[(hb * 2 + (kh ^ 1)) * 128 + 64 + lane];
     const bf16x8_t pk[4] = {kh == 0 ? pb[0] : px0, kh == 0 ? pb[1] : px1,
                             kh == 0 ? px0 : pb[0], kh == 0 ? px1 : pb[1]};
 
@@ -252,7 +288,17 @@ attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = o[dt][g * 4 + j] * inv;
       const int c0 = kh * (AD / 2) + dt * 32 + g * 8 + half * 4;
-      rope_chunk<4>(v, c0, AD, a.r, -qpos, inv_freq);
+      if (c0 + 4 > rope0) {  // counter-rotation: the same angle, negated (eq. 26)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          if (c0 + i >= rope0) {
+            const int pr = (c0 + i - rope0) >> 1;
+            const float c = rope_c[pr], sn = rope_s[pr], x = v[i], y = v[i + 1];
+            v[i] = x * c + y * sn;
+            v[i + 1] = -x * sn + y * c;
+          }
+        }
+      }
       Chunk<bf16_t>::store<4>(orow + c0, v);
     }
   }
