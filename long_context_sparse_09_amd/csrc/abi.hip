@@ -1,5 +1,6 @@
 // Host side of the dsv4attn C ABI: argument validation, kernel dispatch, status reporting.
 // Declarations and argument meaning: include/dsv4attn.h.
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -148,12 +149,13 @@ static int attend_common(dsv4::AttendArgs& a, void* stream, const char* name) {
   REQUIRE(a.window >= 1, "window must be >= 1");
   if (int rc = check_rope(a.r, a.D, a.theta)) return rc;
   if (a.scale <= 0.f) a.scale = 1.0f / sqrtf(static_cast<float>(a.D));
+  for (int i = 0; i < a.r / 2; ++i) a.inv_freq[i] = pow(a.theta, -2.0 * i / a.r);
   if (a.B == 0 || a.T == 0) return ok();
   REQUIRE(a.q && a.kv_win && a.kv_pos0 && a.sink && a.q_pos0 && a.out, "null required pointer");
   REQUIRE(a.N_cap == 0 || a.pool, "pool required when N_cap > 0");
   REQUIRE(aligned16(a.q) && aligned16(a.kv_win) && aligned16(a.out) && (!a.pool || aligned16(a.pool)),
           "pointers must be 16-byte aligned");
-  if (!dsv4::attend_fast(a.H, a.D, a.r, a.dtype)) {
+  if (!dsv4::attend_uses_fast(a)) {
     if (a.D > 4096) return fail(DSV4_ERR_UNSUPPORTED, "D=%d above 4096 for the generic kernel", a.D);
     const long long max_keys = static_cast<long long>(a.window) + (a.csa ? a.k : a.N_cap);
     if (max_keys > dsv4::attend_generic_max_keys())
@@ -172,7 +174,8 @@ int csa_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
   if (k > 4096) return fail(DSV4_ERR_UNSUPPORTED, "k %d above 4096", k);
   REQUIRE(B == 0 || T == 0 || topk_idx, "null topk_idx");
   dsv4::AttendArgs a{q, kv_win, kv_pos0, S_kv, pool, N_cap, topk_idx, k, nullptr, 1, sink, q_pos0,
-                     out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, true};
+                     out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, true,
+                     {}};
   return attend_common(a, stream, "csa_attend");
 }
 
@@ -183,7 +186,8 @@ int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
                void* stream) {
   REQUIRE(m_hca >= 1, "m_hca must be >= 1");
   dsv4::AttendArgs a{q, kv_win, kv_pos0, S_kv, pool, N_cap, nullptr, 0, n_pool, m_hca, sink, q_pos0,
-                     out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, false};
+                     out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, false,
+                     {}};
   return attend_common(a, stream, "hca_attend");
 }
 

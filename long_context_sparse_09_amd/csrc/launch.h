@@ -43,6 +43,7 @@ struct AttendArgs {
   float scale;
   int dtype;
   bool csa;
+  double inv_freq[128];  // theta^(-2i/r), i < r/2, formed on the host in double precision
 };
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
@@ -50,6 +51,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 // Whether the MFMA fast paths cover a shape (otherwise the generic kernels run).
 bool index_scores_fast(int nI, int cI, int dtype);
 bool attend_fast(int H, int D, int r, int dtype);
+bool attend_uses_fast(const AttendArgs& a);
 // Keys one query may see at most (sizes the generic attention kernel's LDS).
 int attend_generic_max_keys();
 
