@@ -12,7 +12,11 @@ fractions.  "roofline" is for the dominant kernel (csa_attend): algorithmic flop
 over the launch's average duration (HIP events on the launch stream).  "cpu_baseline" is the
 fp64 CPU oracle timed on this host's cores over a bounded sample of the same workload.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--copy-calib MiB]
+
+--copy-calib launches one plain device-to-device copy of that many MiB before the timed work,
+so that a counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) sees a kernel of known traffic
+to scale the attention kernel's counters by.
 """
 from __future__ import annotations
 
@@ -264,7 +268,7 @@ def run_decode(torch, steps, warmup):
 
 # ----------------------------------------------------------------------------- CPU oracle
 
-def cpu_baseline(n_sample=384):
+def cpu_baseline(n_sample=640):
     """The fp64 oracle on this host: full pooling of all 8192 tokens plus index / top-k /
     attention for n_sample queries spread over the sequence; extrapolated to all queries."""
     import oracle
@@ -311,6 +315,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA / decode workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
+                    help="launch one device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -319,6 +325,15 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calib > 0:
+        n = args.copy_calib << 18  # fp32 elements
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written")
+        del src, dst
     w, wall, kern = run_csa_prefill(torch, args.steps, args.warmup)
     extra = {}
     if not args.no_extra:

@@ -10,31 +10,37 @@
 // visibility w < (t+1)//m.
 //
 // Work decomposition
-//   * Persistent workgroups (one per CU) walk their queries as one stream of 32-key tiles.
-//     While a query's last tile computes, the next query's first tile is already being
-//     gathered and its Q rows are loading, so per-query set-up overlaps compute.
+//   * Persistent workgroups (one per CU) walk their queries as one stream of 32-key tiles:
+//     the window rows of a query, then its selected (CSA) or visible (HCA) pool rows.
+//   * Nine wavefronts in three roles, pipelined by one tile:
+//       - gather (wave 8): moves each tile's 32 key rows (1 KB each) from global memory
+//         straight into LDS (global_load_lds), three tiles ahead, into a ring of four
+//         tile buffers.  A vector-memory issue stalls the issuing wave at the CU's fill rate,
+//         so every gather sits in this one wave;
+//       - score (waves 0..3, (hb, kh)): heads [32hb, 32hb+32), channels [256kh, 256kh+256).
+//         Partial S^T = K[:, ch kh] . Q^T[ch kh] on v_mfma_f32_32x32x16_bf16 (A = 32 key rows
+//         from LDS, B = its half of the rotated Q in registers); the two waves of a head block
+//         swap partials through LDS, run the same online softmax, and publish P (bf16) and
+//         the rescale factor of the running max for the tile;
+//       - value (waves 4..7, (hb, kh)): O^T[ch kh, heads hb] += V^T . P^T, with V^T read from
+//         the same row-major tile through ds_read_tr16_b64 (K = V is stored once) and P^T
+//         taken from LDS in exactly the B-operand layout the score waves produced it in.
+//     In step s the score waves work on tile s+1, the value waves on tile s and the gather
+//     wave fills tile s+3; a score wave and a value wave share each SIMD, so one's matrix work
+//     covers the other's LDS and softmax latency.  Two workgroup barriers per step: X (tile
+//     s+1 landed, P(s) published, the buffer of tile s-1 free) and Y (partial logits
+//     exchanged).
+//   * Online softmax in the log2 domain; the running max moves only when a logit exceeds it
+//     by 2^8 (lazy rescale).  The state starts from the sink: max = s_h, sum = 1, value 0.
+//   * RoPE angles are formed per lane in double precision (position x frequency, reduced to
+//     turns) and fed to the hardware sin / cos, for the Q rotation and the output
+//     counter-rotation alike.
+//   * LDS rows are 1024 B with their 16-byte chunks XOR-swizzled per row (chunk c of row r
+//     sits at c ^ f(r), f(r) = 4(r mod 4) + ((r >> 2) mod 4)), so the 16-row b128 reads of
+//     QK^T and the 4-row transposing reads of PV each touch 64 distinct banks.
 //   * Query order: heaviest first, and each round hands G/8 consecutive queries to the G/8
 //     workgroups of one XCD, so the window rows that neighbouring queries share are fetched
-//     into that XCD's L2 once.  Q is loaded and the output stored non-temporally, keeping the
-//     pool and window rows resident in L2.
-//   * 4 wavefronts; wave (hb, kh) owns heads [32hb, 32hb+32) and channels [256kh, 256kh+256).
-//   * Gather: a tile's 32 key rows (window rows, then the selected / visible pool rows) go
-//     straight from global memory into LDS (global_load_lds, one 1 KB row per wave
-//     instruction), double-buffered.  Row addresses come from one vector op, read out per row
-//     with readlane.
-//   * QK^T is split over channels: wave (hb, kh) forms the partial S^T = K[:, ch kh] .
-//     Q^T[ch kh] (v_mfma_f32_32x32x16_bf16; A = 32 key rows from LDS, B = its half of the
-//     rotated Q, kept in registers), the two waves of a head block swap partials through LDS,
-//     and both then hold the same full logits (each lane: 16 keys of ONE head).  They run the
-//     same online softmax, so no further exchange is needed.
-//   * The S^T accumulator layout is exactly the B operand of O^T = V^T . P^T, so P goes from
-//     accumulator to operand in registers; V^T (A operand) comes from the same row-major tile
-//     through ds_read_tr16_b64 (transposing 4 x 16 LDS reads): K = V is stored once.
-//   * The running max is moved only when a logit exceeds it by 2^8 (lazy rescale).  The state
-//     starts from the sink: max = s_h, sum = 1, value 0.
-//   * LDS rows are 1024 B with their 16-byte chunks XOR-swizzled per row (chunk c of row r
-//     sits at c ^ f(r), f(r) = 2(r mod 4) + ((r >> 2) mod 2)), so the 8-row b128 reads of QK^T
-//     and the 4-row transposing reads of PV each touch distinct banks.
+//     into that XCD's L2 once.  Q is loaded and the output stored non-temporally.
 #include "common.h"
 #include "launch.h"
 
@@ -49,51 +55,129 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
 namespace {
 
-constexpr int AH = 64;                   // query heads
-constexpr int AD = 512;                  // head_dim
-constexpr int ANK = 32;                  // keys per tile
-constexpr int APITCH = AD * 2;           // LDS bytes per key row (swizzled, no pad)
-constexpr int ATILE = ANK * APITCH;      // bytes per tile buffer
-constexpr int ATILES_BYTES = 2 * ATILE;  // double buffer
-constexpr int AXS_BYTES = 2 * 4 * 16 * 64 * 4;  // partial-logit exchange: [parity][hb,kh][16][64]
-constexpr float kLazy = 8.f;             // log2-domain headroom before the running max moves
-constexpr int kMaxTopk = 1024;           // key-list capacity per buffer on this path
-constexpr int kMaxDynLds = ATILES_BYTES + AXS_BYTES + 2 * kMaxTopk * 4;
+constexpr int AH = 64;                     // query heads
+constexpr int AD = 512;                    // head_dim
+constexpr int ANK = 32;                    // keys per tile
+constexpr int APITCH = AD * 2;             // LDS bytes per key row (swizzled, no pad)
+constexpr int ATILE = ANK * APITCH;        // bytes per tile buffer
+constexpr int NSLOT = 4;                   // tile ring
+constexpr int XS_OFF = NSLOT * ATILE;      // partial-logit exchange: [score wave][4][64] f32x4
+constexpr int P_OFF = XS_OFF + 4 * 4096;   // P tiles: [parity][hb][16-key half][64] bf16x8
+constexpr int AL_OFF = P_OFF + 2 * 2 * 2 * 64 * 16;  // rescale factors: [parity][64 heads]
+constexpr int LS_OFF = AL_OFF + 2 * 64 * 4;          // softmax sums at a query's end: [parity][64]
+constexpr int KL_OFF = LS_OFF + 2 * 64 * 4;          // gather wave's key list (CSA)
+constexpr int kMaxTopk = 1024;                       // key-list capacity on this path
+constexpr int NK_OFF = KL_OFF + kMaxTopk * 4;        // key counts of queries [j % 8]
+constexpr int kLdsBytes = NK_OFF + 8 * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+constexpr float kLazy = 8.f;               // log2-domain headroom before the running max moves
+constexpr double kInv2Pi = 0.15915494309189533576888376337251;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// LDS row swizzle: 16-byte chunk c of key row r sits at chunk c ^ swz(r).  swz is a
+// bijection on every 16 aligned rows (the 16 lanes of a b128 read of QK^T hit 16 different
+// bank groups) and, on every 4 aligned rows, differs in bits 2-3 only (the 4 rows x 4
+// chunks of a transposing read of PV hit 16 different bank groups too).
+__device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 
-// Per-query description, identical in every thread of the workgroup.
-struct QDesc {
-  int b, t, r0, n_win, n_keys, n_tiles, buf;
+// Buffer resources: global memory is read and written through buffer instructions (SGPR
+// descriptor + SGPR offset + one 32-bit VGPR lane offset).  A memory instruction that takes
+// a 64-bit VGPR address per lane issues far more slowly while other waves on the SIMD keep
+// the matrix core busy; the buffer form does not.  Reads past num_records return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer
+constexpr unsigned kOutOfRange = 0xFFFFF000u;  // row offset beyond every descriptor: reads zeros
+__device__ __forceinline__ rsrc_t make_rs(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+constexpr int kNT = 2;  // cache policy bits of the buffer instructions: non-temporal
+
+// Partner value across the two 32-lane halves (lane l <-> lane l ^ 32), combined.
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// cos / sin of angle (pos * inv_freq) for one rotary pair: the product is reduced to turns in
+// double precision, the hardware sin / cos take turns.
+__device__ __forceinline__ void rope_pair(double pos, double inv_freq, float& c, float& s) {
+  const double turns = pos * inv_freq * kInv2Pi;
+  const float frac = static_cast<float>(turns - rint(turns));
+  c = __builtin_amdgcn_cosf(frac);
+  s = __builtin_amdgcn_sinf(frac);
+}
+
+// Per-query description, computed identically by every wave that needs it.
+struct QInfo {
+  int b, t, r0, n_win, n_keys, n_tiles;
   long long p;
 };
 
 }  // namespace
 
+// Every field is uniform across the wave; keep it in scalar registers.
+__device__ __forceinline__ QInfo uniform(const QInfo& d) {
+  QInfo u;
+  u.b = __builtin_amdgcn_readfirstlane(d.b);
+  u.t = __builtin_amdgcn_readfirstlane(d.t);
+  u.r0 = __builtin_amdgcn_readfirstlane(d.r0);
+  u.n_win = __builtin_amdgcn_readfirstlane(d.n_win);
+  u.n_keys = __builtin_amdgcn_readfirstlane(d.n_keys);
+  u.n_tiles = __builtin_amdgcn_readfirstlane(d.n_tiles);
+  const unsigned long long pu = static_cast<unsigned long long>(d.p);
+  u.p = static_cast<long long>((static_cast<unsigned long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(pu >> 32))) << 32) |
+                               __builtin_amdgcn_readfirstlane(static_cast<unsigned>(pu)));
+  return u;
+}
+
+// Position, window rows and (HCA) visible pool entries of query qid; n_keys / n_tiles are
+// completed by set_keys() once the compressed-key count is known.
+template <bool CSA>
+__device__ __forceinline__ QInfo query_geom(const AttendArgs& a, int qid) {
+  QInfo d;
+  d.b = qid / a.T;
+  d.t = qid % a.T;
+  d.p = static_cast<long long>(a.q_pos0[d.b]) + d.t;
+  const long long lo = max(0LL, d.p - a.window + 1);
+  d.r0 = static_cast<int>(max(lo - a.kv_pos0[d.b], 0LL));
+  const int r1 = static_cast<int>(min(d.p + 1 - a.kv_pos0[d.b], static_cast<long long>(a.S_kv)));
+  d.n_win = max(0, r1 - d.r0);
+  d.n_keys = d.n_win;
+  if constexpr (!CSA) {
+    long long v = a.N_cap > 0 ? (d.p + 1) / a.m_hca : 0;
+    v = min(v, static_cast<long long>(a.n_pool ? a.n_pool[d.b] : a.N_cap));
+    v = min(v, static_cast<long long>(a.N_cap));
+    d.n_keys += static_cast<int>(max(v, 0LL));
+  }
+  d.n_tiles = max(1, (d.n_keys + ANK - 1) / ANK);  // an empty query still runs one masked tile
+  return uniform(d);
+}
+
+__device__ __forceinline__ void set_keys(QInfo& d, int n_cmp) {
+  d.n_keys = d.n_win + n_cmp;
+  d.n_tiles = max(1, (d.n_keys + ANK - 1) / ANK);
+}
+
 template <bool CSA, int R>  // R = rotary channels, 0 or 64 (compile-time: only those chunks move)
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(576, 576), amdgpu_waves_per_eu(3, 3)))
 attend_mfma_kernel(AttendArgs a) {
   static_assert(R == 0 || R == 64, "rotary width on this path");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  unsigned char* tiles = lds;
-  f32x4_t* xs = reinterpret_cast<f32x4_t*>(lds + ATILES_BYTES);           // [2][4][4][64]
-  int* klist = reinterpret_cast<int*>(lds + ATILES_BYTES + AXS_BYTES);    // CSA: [2][k]
-  __shared__ float rope_c[2][kMaxRope / 2], rope_s[2][kMaxRope / 2];
-  __shared__ int wave_tot[4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
-  const int hb = wave & 1, kh = wave >> 1;
-  const int head = hb * 32 + l32;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: roles are per wave
   const int n_q = a.B * a.T;
   const int G = gridDim.x;
-  const float c2 = a.scale * kLog2e;  // logits in the log2 domain
-  const float sink2 = a.sink[head] * kLog2e;
   const bf16_t* qbase = static_cast<const bf16_t*>(a.q);
+  int* nk = reinterpret_cast<int*>(lds + NK_OFF);  // compressed-key counts of queries [j % 8]
 
   // j-th query of this workgroup, as a rank in the heaviest-first order.  Workgroups are
   // dealt to the 8 XCDs round-robin; with G a multiple of 8, round j gives XCD x the ranks
@@ -101,325 +185,385 @@ attend_mfma_kernel(AttendArgs a) {
   const int g = static_cast<int>(blockIdx.x);
   const int slot = (G % 8) == 0 ? (g % 8) * (G / 8) + g / 8 : g;
   const int n_mine = (n_q - slot + G - 1) / G;
+  auto qid_of = [&](int j) { return n_q - 1 - (j * G + slot); };
 
-  // ---- per-query set-up: position, window rows, key list, rope table (all threads) ----
-  auto prepare = [&](int j, QDesc& d, int buf) {
-    const int qid = n_q - 1 - (j * G + slot);
-    d.b = qid / a.T;
-    d.t = qid % a.T;
-    d.buf = buf;
-    d.p = static_cast<long long>(a.q_pos0[d.b]) + d.t;
-    const long long lo = max(0LL, d.p - a.window + 1);
-    d.r0 = static_cast<int>(max(lo - a.kv_pos0[d.b], 0LL));
-    const int r1 = static_cast<int>(min(d.p + 1 - a.kv_pos0[d.b], static_cast<long long>(a.S_kv)));
-    d.n_win = max(0, r1 - d.r0);
-    __syncthreads();  // earlier readers of klist[buf] / rope[buf] are done
-    if (tid < R / 2) {  // one (cos, sin) per rotary pair: angle in double, reduced mod 2pi
-      const double turns = static_cast<double>(d.p + a.pos_off) * a.inv_freq[tid] *
-                           0.15915494309189533576888376337251;  // 1 / (2 pi)
-      const float frac = static_cast<float>(turns - rint(turns));  // in [-1/2, 1/2]
-      rope_c[buf][tid] = __builtin_amdgcn_cosf(frac);  // hardware sin/cos take turns
-      rope_s[buf][tid] = __builtin_amdgcn_sinf(frac);
-    }
-    int n_cmp;
-    if constexpr (CSA) {
-      const int* idx = a.topk_idx + (static_cast<size_t>(d.b) * a.T + d.t) * a.k;
-      int* kl = klist + buf * a.k;
-      int base = 0;
-      for (int c0 = 0; c0 < a.k; c0 += 256) {
-        const int i = c0 + tid;
-        const int e = i < a.k ? idx[i] : -1;
-        const bool v = e >= 0 && e < a.N_cap;
-        int tot;
-        const int pos = base + block_excl_count<256>(v, &tot, wave_tot);
-        if (v) kl[pos] = e;
-        base += tot;
+  if (wave == 8) {
+    // ------------------------------------------------------------------ gather wave
+    __builtin_amdgcn_s_setprio(3);  // its issue slots go first: the other waves wait on its tiles
+    const bf16_t* win0 = static_cast<const bf16_t*>(a.kv_win);
+    const bf16_t* pool0 = static_cast<const bf16_t*>(a.pool);
+    int* kl = reinterpret_cast<int*>(lds + KL_OFF);
+    int iq = 0, it = 0;  // issue cursor: query rank, tile
+    QInfo qi;
+    unsigned voff[16];  // lane offset of a row whose chunks are XOR-ed with j
+#pragma unroll
+    for (int j = 0; j < 16; ++j) voff[j] = static_cast<unsigned>(lane ^ j) << 4;
+    auto load_query = [&](int j) {
+      qi = query_geom<CSA>(a, qid_of(j));
+      if constexpr (CSA) {  // compact the valid entries, in order
+        const rsrc_t idx_rs = make_rs(a.topk_idx + (static_cast<size_t>(qi.b) * a.T + qi.t) * a.k,
+                                      static_cast<unsigned>(a.k) * 4u);
+        int base = 0;
+        for (int c0 = 0; c0 < a.k; c0 += 64) {
+          const int i = c0 + lane;
+          const int ld = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(idx_rs, static_cast<unsigned>(i) * 4u, 0, 0));
+          const int e = i < a.k ? ld : -1;
+          const bool v = e >= 0 && e < a.N_cap;
+          const unsigned long long m = __ballot(v);
+          const int pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
+          if (v) kl[pos] = e;
+          base += __popcll(m);
+        }
+        set_keys(qi, base);
       }
-      n_cmp = base;
+      if (lane == 0) nk[j & 7] = qi.n_keys - qi.n_win;  // compressed keys of query j
+    };
+    unsigned rlo = 0, rhi = 0;
+    auto tile_addr = [&]() {  // lane l < 32: address of key it*32 + l of query iq
+      const int x = it * ANK + (lane & 31);
+      const bf16_t* row;
+      if (x < qi.n_keys) {
+        if (x < qi.n_win) {
+          row = win0 + (static_cast<size_t>(qi.b) * a.S_kv + qi.r0 + x) * AD;
+        } else {
+          const int e = CSA ? kl[x - qi.n_win] : x - qi.n_win;
+          row = pool0 + (static_cast<size_t>(qi.b) * a.N_cap + e) * AD;
+        }
+      } else {  // masked filler: the query's own first row (in bounds, finite)
+        row = qbase + (static_cast<size_t>(qi.b) * a.T + qi.t) * AH * AD;
+      }
+      const unsigned long long rp = reinterpret_cast<unsigned long long>(row);
+      rlo = static_cast<unsigned>(rp);
+      rhi = static_cast<unsigned>(rp >> 32);
+    };
+    auto issue_half = [&](int h, int sl) {  // rows 16h .. 16h + 15 into tile buffer sl
+      unsigned char* tb = lds + sl * ATILE;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = h * 16 + i;
+        const unsigned lo32 = __builtin_amdgcn_readlane(rlo, r);
+        const unsigned hi32 = __builtin_amdgcn_readlane(rhi, r);
+        const unsigned char* src = reinterpret_cast<const unsigned char*>(
+            (static_cast<unsigned long long>(hi32) << 32) | lo32);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + voff[swz(r)]),
+                                         (lds_void*)(tb + r * APITCH), 16, 0, 0);
+      }
+    };
+    int n_issued = 0;
+    bool have = true;  // the issue cursor points at a tile
+    auto advance = [&]() {
+      ++n_issued;
+      if (++it < qi.n_tiles) return;
+      it = 0;
+      if (++iq >= n_mine) {
+        have = false;
+        return;
+      }
+      load_query(iq);
+    };
+
+    load_query(0);
+    // prologue: tiles 0 and 1
+    tile_addr();
+    issue_half(0, 0);
+    issue_half(1, 0);
+    advance();
+    if (have) {
+      tile_addr();
+      issue_half(0, 1);
+      issue_half(1, 1);
+      advance();
+      __builtin_amdgcn_s_waitcnt(0x8F70);  // vmcnt(32): tile 0 has landed
     } else {
-      long long v = a.N_cap > 0 ? (d.p + 1) / a.m_hca : 0;
-      v = min(v, static_cast<long long>(a.n_pool ? a.n_pool[d.b] : a.N_cap));
-      v = min(v, static_cast<long long>(a.N_cap));
-      n_cmp = static_cast<int>(max(v, 0LL));
+      __builtin_amdgcn_s_waitcnt(0);
     }
-    d.n_keys = d.n_win + n_cmp;
-    d.n_tiles = max(1, (d.n_keys + ANK - 1) / ANK);  // an empty query still runs one masked tile
-    __syncthreads();
-  };
-
-  const bf16_t* win0 = static_cast<const bf16_t*>(a.kv_win);
-  const bf16_t* pool0 = static_cast<const bf16_t*>(a.pool);
-  // Gather of tile `it` of query d into tile buffer `tbuf`, in two steps: tile_addr() forms,
-  // in lane l < 32, the address of key it*32 + l; issue_row(p) then moves row p*4 + wave
-  // (1 KB, read out with readlane) straight into LDS, every lane fetching the logical chunk
-  // that belongs at its physical (swizzled) LDS position.  The 8 row moves of a wave are
-  // interleaved with the QK^T MFMAs so that issue stalls overlap matrix work.
-  unsigned rlo = 0, rhi = 0;
-  unsigned char* gtb = tiles;
-  auto tile_addr = [&](const QDesc& d, int it, int tbuf) {
-    const int x = it * ANK + l32;
-    const bf16_t* row;
-    if (x < d.n_keys) {
-      if (x < d.n_win) {
-        row = win0 + (static_cast<size_t>(d.b) * a.S_kv + d.r0 + x) * AD;
+    // step s: fill tile s + 3 (its buffer held tile s - 1), then wait for tile s + 2
+    for (int s = -1;; ++s) {
+      __syncthreads();  // X(s)
+      const bool issuing = have;
+      const int sl = n_issued % NSLOT;
+      if (issuing) {
+        tile_addr();
+        issue_half(0, sl);
+      }
+      __syncthreads();  // Y(s)
+      if (issuing) {
+        issue_half(1, sl);
+        advance();
+        __builtin_amdgcn_s_waitcnt(0x8F70);  // vmcnt(32)
       } else {
-        const int e = CSA ? klist[d.buf * a.k + x - d.n_win] : x - d.n_win;
-        row = pool0 + (static_cast<size_t>(d.b) * a.N_cap + e) * AD;
+        __builtin_amdgcn_s_waitcnt(0);
       }
-    } else {  // masked filler: the query's own first row (in bounds, finite)
-      row = qbase + (static_cast<size_t>(d.b) * a.T + d.t) * AH * AD;
+      if (!have && s + 1 >= n_issued) break;  // step n_tiles - 1 was the last
     }
-    const unsigned long long rp = reinterpret_cast<unsigned long long>(row);
-    rlo = static_cast<unsigned>(rp);
-    rhi = static_cast<unsigned>(rp >> 32);
-    gtb = tiles + tbuf * ATILE;
-  };
-  auto issue_row = [&](int pass) {
-    const int r = pass * 4 + wave;
-    const unsigned lo32 = __builtin_amdgcn_readlane(rlo, r);
-    const unsigned hi32 = __builtin_amdgcn_readlane(rhi, r);
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(
-        (static_cast<unsigned long long>(hi32) << 32) | lo32);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + ((lane ^ swz(r)) << 4)),
-                                     (lds_void*)(gtb + r * APITCH), 16, 0, 0);
-  };
-  auto issue_tile = [&](const QDesc& d, int it, int tbuf) {
-    tile_addr(d, it, tbuf);
-#pragma unroll
-    for (int pass = 0; pass < ANK / 4; ++pass) issue_row(pass);
-  };
-
-  // This wave's half of Q^T (B operand): head hb*32 + l32, channels kh*256 + ks*16 + half*8
-  constexpr int NKS = AD / 2 / 16;
-  bf16x8_t qf[NKS];
-  auto load_q = [&](const QDesc& d) {
-    const bf16_t* qrow = qbase + ((static_cast<size_t>(d.b) * a.T + d.t) * AH + head) * AD +
-                         kh * (AD / 2) + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = __builtin_bit_cast(
-          bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(qrow + ks * 16)));
-  };
-  // rotary channels 448..511 = the last R/16 chunks of the kh = 1 half
-  auto rotate_q = [&](const QDesc& d) {
-    if (R == 0 || kh == 0) return;
-#pragma unroll
-    for (int ks = NKS - R / 16; ks < NKS; ++ks) {
-      const int pr0 = (ks * 16 + half * 8 - (AD / 2 - R)) >> 1;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float c = rope_c[d.buf][pr0 + i / 2], sn = rope_s[d.buf][pr0 + i / 2];
-        const float xv = static_cast<float>(qf[ks][i]), yv = static_cast<float>(qf[ks][i + 1]);
-        qf[ks][i] = static_cast<__bf16>(xv * c - yv * sn);
-        qf[ks][i + 1] = static_cast<__bf16>(xv * sn + yv * c);
-      }
-    }
-  };
-
-  // lane-constant LDS offsets of the swizzled layout
-  int qk_off[4];  // QK^T A operand: row l32, chunk kh*32 + 2*(ks%4) + half (+ 8*(ks/4))
-  {
-    const int f = swz(l32);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      qk_off[jj] = l32 * APITCH + kh * 4 * 128 + (((2 * jj + half) ^ f) << 4);
+    return;
   }
-  // PV transposing reads: rows 16ss + 4*half + n16/4 (+8), channels kh*256 + dt*32 + dh*16
-  // + 4*(n16%4); the 16-byte chunk of that column is XOR-ed with f = swz(row) = 2(n16/4)+half
-  int tr_off[2];
+
+  const int half = lane >> 5, l32 = lane & 31;
+  const int role_w = wave & 3;
+  const int hb = role_w & 1, kh = role_w >> 1;
+  const int head = hb * 32 + l32;
+  constexpr int NKS = AD / 2 / 16;  // channel steps of QK^T per wave
+  constexpr int NDT = AD / 2 / 32;  // output channel tiles per wave
+  bf16x8_t* pbuf = reinterpret_cast<bf16x8_t*>(lds + P_OFF);  // [parity][hb][ss][64]
+  float* alph = reinterpret_cast<float*>(lds + AL_OFF);        // [parity][64 heads]
+  float* lsum = reinterpret_cast<float*>(lds + LS_OFF);        // [parity][64 heads]
+
+  if (wave < 4) {
+    // ------------------------------------------------------------------ score waves
+    const float c2 = a.scale * kLog2e;  // logits in the log2 domain
+    const float sink2 = a.sink[head] * kLog2e;
+    // This wave's half of Q^T (B operand): head, channels kh*256 + ks*16 + half*8
+    bf16x8_t qf[NKS];
+    const unsigned qvoff = static_cast<unsigned>((head * AD + kh * (AD / 2) + half * 8) * 2);
+    auto load_q = [&](const QInfo& d) {
+      const rsrc_t q_rs = make_rs(qbase + (static_cast<size_t>(d.b) * a.T + d.t) * AH * AD, AH * AD * 2);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qvoff + ks * 32, 0, kNT));
+    };
+    // rotary channels 448..511 = the last R/16 chunks of the kh = 1 half; pair index
+    // (channel - (512 - R)) / 2
+    auto rotate_q = [&](const QInfo& d) {
+      if (R == 0 || kh == 0) return;
+      const double pos = static_cast<double>(d.p + a.pos_off);
+#pragma unroll
+      for (int ks = NKS - R / 16; ks < NKS; ++ks) {
+        const int pr0 = (ks * 16 + half * 8 - (AD / 2 - R)) >> 1;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          float c, sn;
+          rope_pair(pos, a.inv_freq[pr0 + i / 2], c, sn);
+          const float xv = static_cast<float>(qf[ks][i]), yv = static_cast<float>(qf[ks][i + 1]);
+          qf[ks][i] = static_cast<__bf16>(xv * c - yv * sn);
+          qf[ks][i + 1] = static_cast<__bf16>(xv * sn + yv * c);
+        }
+      }
+    };
+    // QK^T A operand of step ks: row l32, chunk kh*32 + 2ks + half, at byte
+    // qk_base ^ (32 ks) (the chunk's low 4 bits are XOR-ed with swz(l32))
+    const int qk_base = l32 * APITCH + kh * (AD / 2) * 2 + ((half ^ swz(l32)) << 4);
+    f32x4_t* xme = reinterpret_cast<f32x4_t*>(lds + XS_OFF) + role_w * 256 + lane;
+    const f32x4_t* xpa = reinterpret_cast<const f32x4_t*>(lds + XS_OFF) + (role_w ^ 2) * 256 + lane;
+
+    int jq = 0, tq = 0;  // cursor: query rank, tile within it
+    QInfo cq = query_geom<CSA>(a, qid_of(0));
+    load_q(cq);
+    float m_run = sink2, l_run = 1.f;
+    f32x16_t sacc;
+    for (int s = -1;; ++s) {
+      __syncthreads();  // X(s): tile s + 1 has landed
+      const bool has = jq < n_mine;  // this step scores tile s + 1
+      const bool first = has && tq == 0;
+      bool last = false;
+      if (has) {
+        if (first) {
+          if constexpr (CSA) set_keys(cq, __builtin_amdgcn_readfirstlane(nk[jq & 7]));
+          rotate_q(cq);
+          m_run = sink2;
+          l_run = 1.f;
+        }
+        last = (tq + 1 == cq.n_tiles);
+        const unsigned char* tb = lds + ((s + 1) % NSLOT) * ATILE;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+        constexpr int PF = 2;
+        bf16x8_t kr[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) kr[i] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * i)));
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8_t kf = kr[ks % PF];
+          if (ks + PF < NKS)
+            kr[ks % PF] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * (ks + PF))));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (last && jq + 1 < n_mine) load_q(query_geom<CSA>(a, qid_of(jq + 1)));  // next Q streams in
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xme[q4 * 64] = f32x4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
+      }
+      __syncthreads();  // Y(s): partials exchanged
+      if (!has) break;
+      {
+        f32x4_t pv4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) pv4[q4] = xpa[q4 * 64];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[4 * q4 + i] += pv4[q4][i];
+      }
+      // online softmax over the tile's 32 keys (lane: head l32, keys (e/4)*8 + half*4 + e%4)
+      const int kbase = tq * ANK + half * 4;
+      float tmax = -INFINITY;
+      if (tq * ANK + ANK > cq.n_keys) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kbase + (e >> 2) * 8 + (e & 3);
+          sacc[e] = key < cq.n_keys ? sacc[e] * c2 : -INFINITY;
+          tmax = fmaxf(tmax, sacc[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sacc[e] *= c2;
+          tmax = fmaxf(tmax, sacc[e]);
+        }
+      }
+      tmax = xhalf_max(tmax);
+      const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float psum = 0.f;
+      bf16x8_t pb;  // this wave publishes keys 16kh .. 16kh + 15 of the tile
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[e] - m_new);
+        psum += pv;
+        if ((e >> 3) == kh) pb[e & 7] = static_cast<__bf16>(pv);
+      }
+      psum = xhalf_sum(psum);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const int par = (s + 1) & 1;
+      pbuf[((par * 2 + hb) * 2 + kh) * 64 + lane] = pb;
+      if (half == 0) {
+        if (kh == 0) alph[par * 64 + head] = alpha;
+        else if (last) lsum[par * 64 + head] = l_run;
+      }
+      if (last) {
+        tq = 0;
+        if (++jq < n_mine) cq = query_geom<CSA>(a, qid_of(jq));
+      } else {
+        ++tq;
+      }
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------------- value waves
+  // PV transposing reads of dim tile dt, key half ss: rows 16ss + 4*half + i (lo) and
+  // + 8 (hi), i = n16/4; channels kh*256 + dt*32 + dh*16 + 4*(n16%4), i.e. chunk
+  // kh*32 + 4dt + j, j = 2dh + (n16%4)/2.  With swz(row) = 4i + (half | 2hi) the chunk's
+  // bits 2-3 become (dt%4) ^ i and bits 0-1 j ^ (half | 2hi): the byte offset is
+  // (tr_lo or tr_hi) ^ (64 (dt%4)), plus 256 (dt/4) and 16 KB ss.
+  int tr_lo, tr_hi;
   {
     const int n16 = lane & 15, dh = (lane >> 4) & 1;
-    const int f = 2 * (n16 >> 2) + half;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-      tr_off[jj] = (4 * half + (n16 >> 2)) * APITCH + kh * 4 * 128 +
-                   (((4 * jj + 2 * dh + ((n16 & 3) >> 1)) ^ f) << 4) + (n16 & 1) * 8;
+    const int i = n16 >> 2, j = 2 * dh + ((n16 & 3) >> 1);
+    const int common = kh * (AD / 2) * 2 + 64 * i + (n16 & 1) * 8;
+    tr_lo = (4 * half + i) * APITCH + common + 16 * (j ^ half);
+    tr_hi = (4 * half + i + 8) * APITCH + common + 16 * (j ^ (half | 2));
   }
-
-  constexpr int NDT = AD / 2 / 32;  // output channel tiles owned by this wave
   f32x16_t o[NDT];
-  float m_run = sink2, l_run = 1.f;
-  auto reset = [&]() {
-    m_run = sink2;
-    l_run = 1.f;
+  int jp = 0, tp = 0;  // cursor: query rank, tile within it
+  QInfo cp = query_geom<CSA>(a, qid_of(0));
+  bf16x8_t pb[2];
+  auto pv_half = [&](const unsigned char* tb, int ss) {  // keys 16ss .. 16ss + 15 of the tile
+    auto vfrag = [&](int dt) {
+      const unsigned char* vb = tb + 16 * ss * APITCH + 256 * (dt >> 2);
+      const int x = 64 * (dt & 3);
+      const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (tr_lo ^ x)));
+      const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (tr_hi ^ x)));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int VPF = 2;
+    bf16x8_t vr[VPF];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int i = 0; i < VPF; ++i) vr[i] = vfrag(i);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x8_t vf = vr[dt % VPF];
+      if (dt + VPF < NDT) vr[dt % VPF] = vfrag(dt + VPF);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ss], o[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-
-  // ---- epilogue of one query: normalise, counter-rotate (eq. 26), store ----
-  // The finished tile buffer (32 KB, free once the workgroup has synchronised) stages the
-  // output so that stores are contiguous: in round hr, wave (hb, kh) writes channels
-  // kh*256 + [128hr, 128hr+128) of its 32 heads (8 KB: row = head, 16 chunks of 16 B, chunk c
-  // of row h at c ^ (h mod 16)) into its quarter, then each store instruction writes 4 heads x
-  // 256 contiguous bytes.
-  auto finish = [&](const QDesc& d, unsigned char* stage) {
-    const float inv = 1.f / l_run;
-    unsigned char* wst = stage + wave * 8192;
-    bf16_t* obase = static_cast<bf16_t*>(a.out) +
-                    ((static_cast<size_t>(d.b) * a.T + d.t) * AH + hb * 32) * AD + kh * (AD / 2);
+  // epilogue of one query: normalise, counter-rotate (eq. 26), store.  A 32-lane swap pairs
+  // the two 4-channel halves so that each lane writes 16 contiguous bytes.
+  const unsigned ovoff = static_cast<unsigned>((head * AD + kh * (AD / 2) + half * 8) * 2);
+  auto finish = [&](const QInfo& d, float inv) {
+    const rsrc_t o_rs = make_rs(static_cast<bf16_t*>(a.out) + (static_cast<size_t>(d.b) * a.T + d.t) * AH * AD,
+                                AH * AD * 2);
+    const double pos = -static_cast<double>(d.p + a.pos_off);  // the same angle, negated
 #pragma unroll
-    for (int hr = 0; hr < 2; ++hr) {
+    for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int dq = 0; dq < NDT / 2; ++dq) {
-        const int dt = hr * (NDT / 2) + dq;
+      for (int gp = 0; gp < 2; ++gp) {
+        unsigned w[2][2];
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int gq = 2 * gp + g2;
           float v[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) v[jj] = o[dt][gq * 4 + jj] * inv;
           const int cl = dt * 32 + gq * 8 + half * 4;  // channel within this wave's half
-          if (R > 0 && kh == 1 && cl >= AD / 2 - R) {  // the same angle, negated
+          if (R > 0 && kh == 1 && cl >= AD / 2 - R) {
             const int pr0 = (cl - (AD / 2 - R)) >> 1;
 #pragma unroll
             for (int i2 = 0; i2 < 4; i2 += 2) {
-              const float c = rope_c[d.buf][pr0 + i2 / 2], sn = rope_s[d.buf][pr0 + i2 / 2];
+              float c, sn;
+              rope_pair(pos, a.inv_freq[pr0 + i2 / 2], c, sn);
               const float xv = v[i2], yv = v[i2 + 1];
-              v[i2] = xv * c + yv * sn;
-              v[i2 + 1] = -xv * sn + yv * c;
+              v[i2] = xv * c - yv * sn;
+              v[i2 + 1] = xv * sn + yv * c;
             }
           }
-          u32x2_t pk2;
-          pk2[0] = pack_bf16x2(v[0], v[1]);
-          pk2[1] = pack_bf16x2(v[2], v[3]);
-          const int chunk = (dq * 4 + gq) ^ (l32 & 15);  // head l32, channels (dq*4+gq)*8 ..
-          *reinterpret_cast<u32x2_t*>(wst + l32 * 256 + chunk * 16 + half * 8) = pk2;
+          w[g2][0] = pack_bf16x2(v[0], v[1]);
+          w[g2][1] = pack_bf16x2(v[2], v[3]);
         }
-      }
-#pragma unroll
-      for (int k2 = 0; k2 < 8; ++k2) {  // lane l: head 4*k2 + l/16, 16-byte chunk l%16
-        const int hh = 4 * k2 + (lane >> 4), ch = lane & 15;
-        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(wst + hh * 256 + ((ch ^ (hh & 15)) << 4));
-        __builtin_nontemporal_store(
-            val, reinterpret_cast<u32x4_t*>(obase + static_cast<size_t>(hh) * AD + hr * 128 + ch * 8));
+        // lanes < 32 collect group 2gp (channels +0..7), lanes >= 32 group 2gp+1
+        const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+        u32x4_t val;
+        val[0] = s0[0];
+        val[1] = s1[0];
+        val[2] = s0[1];
+        val[3] = s1[1];
+        // lanes >= 32 write group 2gp + 1: their half * 8 channels are part of ovoff
+        __builtin_amdgcn_raw_buffer_store_b128(val, o_rs, ovoff + (dt * 32 + 2 * gp * 8) * 2, 0, kNT);
       }
     }
   };
 
-  QDesc cur, nxt;
-  prepare(0, cur, 0);
-  load_q(cur);
-  issue_tile(cur, 0, 0);
-  int j = 0, it = 0, tbuf = 0, par = 0;
-
-  for (;;) {
-    if (it == 0) {  // a new query starts: set up the following one, then this one's Q and state
-      if (j + 1 < n_mine) prepare(j + 1, nxt, cur.buf ^ 1);
-      rotate_q(cur);
-      reset();
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's gather of the current tile has landed
-    __syncthreads();                // ... and every wave's; the other tile buffer is free
-    const bool last = (it + 1 == cur.n_tiles);
-    const bool more = (j + 1 < n_mine);
-    const bool fetch = !last || more;
-    if (fetch) tile_addr(last ? nxt : cur, last ? 0 : it + 1, tbuf ^ 1);
-    const unsigned char* tb = tiles + tbuf * ATILE;
-
-    // partial S^T (32 keys x 32 heads) over this wave's 256 channels; K fragments run 4 ahead,
-    // one gather row move after every second MFMA
-    f32x16_t s;
+  for (int s = -1;; ++s) {
+    __syncthreads();  // X(s): P(s) and the rescale factor are published
+    const bool has = s >= 0 && jp < n_mine;  // this step accumulates tile s
+    const unsigned char* tb = lds + ((s + NSLOT) % NSLOT) * ATILE;
+    if (has) {
+      if (tp == 0) {
+        if constexpr (CSA) set_keys(cp, __builtin_amdgcn_readfirstlane(nk[jp & 7]));
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.f;
-    {
-      constexpr int PF = 4;
-      bf16x8_t kr[PF];
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < PF; ++i) kr[i] = *reinterpret_cast<const bf16x8_t*>(tb + qk_off[i]);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8_t kf = kr[ks % PF];
-        if (ks + PF < NKS)
-          kr[ks % PF] = *reinterpret_cast<const bf16x8_t*>(tb + qk_off[(ks + PF) & 3] + ((ks + PF) >> 2) * 128);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
-        if ((ks & 1) && fetch) issue_row(ks >> 1);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
       }
-    }
-    if (last && more) load_q(nxt);  // the next query's Q streams in behind this tile
-
-    // swap partial logits with the other channel half of this head block
-    f32x4_t* xme = xs + ((par * 4 + hb * 2 + kh) * 4) * 64 + lane;
-    const f32x4_t* xpa = xs + ((par * 4 + hb * 2 + (kh ^ 1)) * 4) * 64 + lane;
+      const int par = s & 1;
+      pb[0] = pbuf[((par * 2 + hb) * 2 + 0) * 64 + lane];
+      pb[1] = pbuf[((par * 2 + hb) * 2 + 1) * 64 + lane];
+      const float alpha = alph[par * 64 + head];
+      if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) xme[q4 * 64] = f32x4_t{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-    __syncthreads();
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4_t pv4 = xpa[q4 * 64];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * q4 + i] += pv4[i];
-    }
-
-    // online softmax over the tile's 32 keys (lane: head l32, keys (e/4)*8 + half*4 + e%4);
-    // both waves of the head block compute the same values
-    const int kbase = it * ANK + half * 4;
-    float tmax = -INFINITY;
-    if (it * ANK + ANK > cur.n_keys) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kbase + (e >> 2) * 8 + (e & 3);
-        s[e] = key < cur.n_keys ? s[e] * c2 : -INFINITY;
-        tmax = fmaxf(tmax, s[e]);
+          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
       }
+      pv_half(tb, 0);
+    }
+    __syncthreads();  // Y(s)
+    if (s < 0) continue;
+    if (!has) break;
+    pv_half(tb, 1);
+    if (tp + 1 == cp.n_tiles) {
+      finish(cp, 1.f / lsum[(s & 1) * 64 + head]);
+      tp = 0;
+      if (++jp < n_mine) cp = query_geom<CSA>(a, qid_of(jp));
+      else break;  // that was the last tile: step n_tiles - 1 is done
     } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[e] *= c2;
-        tmax = fmaxf(tmax, s[e]);
-      }
+      ++tp;
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.f;
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pv = __builtin_amdgcn_exp2f(s[e] - m_new);
-      psum += pv;
-      pb[e >> 3][e & 7] = static_cast<__bf16>(pv);
-    }
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    if (__ballot(m_new != m_run)) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-    }
-    m_run = m_new;
-
-    // O^T (32 channels x 32 heads per tile dt) += V^T (32 channels x 16 key slots) . P^T
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const unsigned char* vb = tb + 16 * ss * APITCH;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const unsigned char* va = vb + tr_off[dt & 1] + (dt >> 1) * 128;
-        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(va));
-        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(va + 8 * APITCH));
-        const bf16x8_t vf = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ss], o[dt], 0, 0, 0);
-      }
-    }
-
-    if (last) {
-      __syncthreads();  // every wave is done with this tile buffer: it stages the output
-      finish(cur, tiles + tbuf * ATILE);
-    }
-    par ^= 1;
-    tbuf ^= 1;
-    if (!last) {
-      ++it;
-      continue;
-    }
-    if (!more) break;
-    cur = nxt;
-    ++j;
-    it = 0;
   }
 }
 
@@ -428,20 +572,21 @@ bool attend_fast(int H, int D, int r, int dtype) {
 }
 
 bool attend_uses_fast(const AttendArgs& a) {
-  return attend_fast(a.H, a.D, a.r, a.dtype) && (!a.csa || a.k <= kMaxTopk);
+  // a batch's window / pool slice must be addressable with 32-bit buffer offsets
+  constexpr long long kMaxRows = (1LL << 22) - 8;
+  return attend_fast(a.H, a.D, a.r, a.dtype) && (!a.csa || a.k <= kMaxTopk) && a.S_kv <= kMaxRows &&
+         a.N_cap <= kMaxRows;
 }
 
 hipError_t launch_attend_generic(const AttendArgs& a, hipStream_t st);
 
 template <bool CSA, int R>
 static hipError_t launch_mfma(const AttendArgs& a, hipStream_t st) {
-  const size_t shmem =
-      ATILES_BYTES + AXS_BYTES + (CSA ? 2 * static_cast<size_t>(a.k) * sizeof(int) : 0);
   static bool attr_set = false;  // per instantiation; setting it again is harmless
   static int n_cu = 0;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_kernel<CSA, R>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDynLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     int dev = 0;
     e = hipGetDevice(&dev);
@@ -452,7 +597,7 @@ static hipError_t launch_mfma(const AttendArgs& a, hipStream_t st) {
   }
   const int n_q = a.B * a.T;
   const unsigned blocks = static_cast<unsigned>(n_q < n_cu ? n_q : n_cu);
-  hipLaunchKernelGGL((attend_mfma_kernel<CSA, R>), dim3(blocks), dim3(256), shmem, st, a);
+  hipLaunchKernelGGL((attend_mfma_kernel<CSA, R>), dim3(blocks), dim3(576), kLdsBytes, st, a);
   return hipGetLastError();
 }
 
