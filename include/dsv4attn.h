@@ -76,7 +76,9 @@ const char* dsv4_last_error(void);
  *   x, gate : [B, S, C] dtype.   bias : [overlap ? 2m : m, C] float32 or NULL.
  *   pool    : [B, N_cap, C] dtype; rows [entry_begin, entry_end) are written, others kept.
  *   Requires 0 <= entry_begin <= entry_end <= N_cap, entry_end * m <= S (every window is
- *   closed), C even and C <= 8192, rope_dim even and <= C, m >= 1.
+ *   closed), C even, rope_dim even and <= min(C, 256), m >= 1 (DSV4_ERR_INVALID otherwise).
+ *   C must be a multiple of 8 up to 2048, or any even C up to 512 (DSV4_ERR_UNSUPPORTED
+ *   otherwise).  Pointers 16-byte aligned.
  */
 int csa_compress(const void* x, const void* gate, const float* bias, void* pool, int B, int S,
                  int C, int m, int overlap, int entry_begin, int entry_end, int N_cap,
