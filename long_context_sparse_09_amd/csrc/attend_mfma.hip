@@ -68,7 +68,8 @@ constexpr int LS_OFF = AL_OFF + 2 * 64 * 4;          // softmax sums at a query'
 constexpr int KL_OFF = LS_OFF + 2 * 64 * 4;          // gather wave's key list (CSA)
 constexpr int kMaxTopk = 1024;                       // key-list capacity on this path
 constexpr int NK_OFF = KL_OFF + kMaxTopk * 4;        // key counts of queries [j % 8]
-constexpr int kLdsBytes = NK_OFF + 8 * 4;
+constexpr int IF_OFF = NK_OFF + 8 * 4;               // RoPE frequencies (double) [32]
+constexpr int kLdsBytes = IF_OFF + 32 * 8;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 constexpr float kLazy = 8.f;               // log2-domain headroom before the running max moves
 constexpr double kInv2Pi = 0.15915494309189533576888376337251;
@@ -114,6 +115,17 @@ __device__ __forceinline__ void rope_pair(double pos, double inv_freq, float& c,
   s = __builtin_amdgcn_sinf(frac);
 }
 
+// Workgroup barrier for LDS hand-offs.  __syncthreads() also drains every outstanding
+// vector-memory operation of the calling wave (its release fence waits for vmcnt 0), which
+// would make the gather wave wait for tiles it has only just issued; here only this wave's
+// LDS operations are drained.  The gather wave orders its tiles with explicit vmcnt waits.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Per-query description, computed identically by every wave that needs it.
 struct QInfo {
   int b, t, r0, n_win, n_keys, n_tiles;
@@ -121,6 +133,12 @@ struct QInfo {
 };
 
 }  // namespace
+
+// Load of a value every lane reads at the same address, through the constant address space:
+// a scalar load, which neither waits for nor is waited on by vector-memory traffic.
+__device__ __forceinline__ int load_uniform(const int* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int*>(reinterpret_cast<uintptr_t>(p));
+}
 
 // Every field is uniform across the wave; keep it in scalar registers.
 __device__ __forceinline__ QInfo uniform(const QInfo& d) {
@@ -144,15 +162,16 @@ __device__ __forceinline__ QInfo query_geom(const AttendArgs& a, int qid) {
   QInfo d;
   d.b = qid / a.T;
   d.t = qid % a.T;
-  d.p = static_cast<long long>(a.q_pos0[d.b]) + d.t;
+  d.p = static_cast<long long>(load_uniform(a.q_pos0 + d.b)) + d.t;
+  const int kv0 = load_uniform(a.kv_pos0 + d.b);
   const long long lo = max(0LL, d.p - a.window + 1);
-  d.r0 = static_cast<int>(max(lo - a.kv_pos0[d.b], 0LL));
-  const int r1 = static_cast<int>(min(d.p + 1 - a.kv_pos0[d.b], static_cast<long long>(a.S_kv)));
+  d.r0 = static_cast<int>(max(lo - kv0, 0LL));
+  const int r1 = static_cast<int>(min(d.p + 1 - kv0, static_cast<long long>(a.S_kv)));
   d.n_win = max(0, r1 - d.r0);
   d.n_keys = d.n_win;
   if constexpr (!CSA) {
     long long v = a.N_cap > 0 ? (d.p + 1) / a.m_hca : 0;
-    v = min(v, static_cast<long long>(a.n_pool ? a.n_pool[d.b] : a.N_cap));
+    v = min(v, static_cast<long long>(a.n_pool ? load_uniform(a.n_pool + d.b) : a.N_cap));
     v = min(v, static_cast<long long>(a.N_cap));
     d.n_keys += static_cast<int>(max(v, 0LL));
   }
@@ -178,6 +197,9 @@ attend_mfma_kernel(AttendArgs a) {
   const int G = gridDim.x;
   const bf16_t* qbase = static_cast<const bf16_t*>(a.q);
   int* nk = reinterpret_cast<int*>(lds + NK_OFF);  // compressed-key counts of queries [j % 8]
+  // RoPE frequencies in LDS (read before the first barrier's release by nobody; written here)
+  double* invf = reinterpret_cast<double*>(lds + IF_OFF);
+  if (wave == 0 && lane < R / 2) invf[lane] = a.inv_freq[lane];
 
   // j-th query of this workgroup, as a rank in the heaviest-first order.  Workgroups are
   // dealt to the 8 XCDs round-robin; with G a multiple of 8, round j gives XCD x the ranks
@@ -280,14 +302,14 @@ attend_mfma_kernel(AttendArgs a) {
     }
     // step s: fill tile s + 3 (its buffer held tile s - 1), then wait for tile s + 2
     for (int s = -1;; ++s) {
-      __syncthreads();  // X(s)
+      lds_barrier();  // X(s)
       const bool issuing = have;
       const int sl = n_issued % NSLOT;
       if (issuing) {
         tile_addr();
         issue_half(0, sl);
       }
-      __syncthreads();  // Y(s)
+      lds_barrier();  // Y(s)
       if (issuing) {
         issue_half(1, sl);
         advance();
@@ -330,11 +352,13 @@ attend_mfma_kernel(AttendArgs a) {
       const double pos = static_cast<double>(d.p + a.pos_off);
 #pragma unroll
       for (int ks = NKS - R / 16; ks < NKS; ++ks) {
-        const int pr0 = (ks * 16 + half * 8 - (AD / 2 - R)) >> 1;
+        const int pr0 = (ks * 16 - (AD / 2 - R)) >> 1;  // pair of this lane: pr0 + 4 half + i/2
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
+          // both candidates at fixed offsets: scalar loads, no vector-memory wait
+          const double f0 = invf[pr0 + i / 2], f1 = invf[pr0 + 4 + i / 2];
           float c, sn;
-          rope_pair(pos, a.inv_freq[pr0 + i / 2], c, sn);
+          rope_pair(pos, half ? f1 : f0, c, sn);
           const float xv = static_cast<float>(qf[ks][i]), yv = static_cast<float>(qf[ks][i + 1]);
           qf[ks][i] = static_cast<__bf16>(xv * c - yv * sn);
           qf[ks][i + 1] = static_cast<__bf16>(xv * sn + yv * c);
@@ -353,7 +377,7 @@ attend_mfma_kernel(AttendArgs a) {
     float m_run = sink2, l_run = 1.f;
     f32x16_t sacc;
     for (int s = -1;; ++s) {
-      __syncthreads();  // X(s): tile s + 1 has landed
+      lds_barrier();  // X(s): tile s + 1 has landed
       const bool has = jq < n_mine;  // this step scores tile s + 1
       const bool first = has && tq == 0;
       bool last = false;
@@ -368,7 +392,7 @@ attend_mfma_kernel(AttendArgs a) {
         const unsigned char* tb = lds + ((s + 1) % NSLOT) * ATILE;
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-        constexpr int PF = 2;
+        constexpr int PF = 6;  // K fragments in flight
         bf16x8_t kr[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i) kr[i] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * i)));
@@ -385,7 +409,7 @@ attend_mfma_kernel(AttendArgs a) {
         for (int q4 = 0; q4 < 4; ++q4)
           xme[q4 * 64] = f32x4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
       }
-      __syncthreads();  // Y(s): partials exchanged
+      lds_barrier();  // Y(s): partials exchanged
       if (!has) break;
       {
         f32x4_t pv4[4];
@@ -461,23 +485,29 @@ attend_mfma_kernel(AttendArgs a) {
   int jp = 0, tp = 0;  // cursor: query rank, tile within it
   QInfo cp = query_geom<CSA>(a, qid_of(0));
   bf16x8_t pb[2];
-  auto pv_half = [&](const unsigned char* tb, int ss) {  // keys 16ss .. 16ss + 15 of the tile
-    auto vfrag = [&](int dt) {
-      const unsigned char* vb = tb + 16 * ss * APITCH + 256 * (dt >> 2);
-      const int x = 64 * (dt & 3);
-      const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (tr_lo ^ x)));
-      const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (tr_hi ^ x)));
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    constexpr int VPF = 2;
-    bf16x8_t vr[VPF];
+  // PV runs as one stream of 16 steps st = 16-key half * NDT + dt, whose V fragments are
+  // read VPF steps ahead (across the Y barrier: the tile is complete from X on).
+  constexpr int VPF = 2;
+  bf16x8_t vr[VPF];
+  auto vfrag = [&](const unsigned char* tb, int st) {
+    const unsigned char* vb = tb + 16 * (st / NDT) * APITCH + 256 * ((st % NDT) >> 2);
+    // the XOR is formed at each read (volatile asm is not hoisted): keeping eight
+    // pre-XOR-ed offsets live would push the accumulators out of registers
+    const int x = 64 * (st & 3);
+    int olo, ohi;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(olo) : "v"(tr_lo), "s"(x));
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(ohi) : "v"(tr_hi), "s"(x));
+    const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + olo));
+    const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + ohi));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pv_steps = [&](const unsigned char* tb, int st0) {  // steps st0 .. st0 + NDT - 1
 #pragma unroll
-    for (int i = 0; i < VPF; ++i) vr[i] = vfrag(i);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x8_t vf = vr[dt % VPF];
-      if (dt + VPF < NDT) vr[dt % VPF] = vfrag(dt + VPF);
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ss], o[dt], 0, 0, 0);
+    for (int i = 0; i < NDT; ++i) {
+      const int st = st0 + i;
+      const bf16x8_t vf = vr[st % VPF];
+      if (st + VPF < 2 * NDT) vr[st % VPF] = vfrag(tb, st + VPF);
+      o[st % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[st / NDT], o[st % NDT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -499,13 +529,14 @@ attend_mfma_kernel(AttendArgs a) {
           float v[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) v[jj] = o[dt][gq * 4 + jj] * inv;
-          const int cl = dt * 32 + gq * 8 + half * 4;  // channel within this wave's half
-          if (R > 0 && kh == 1 && cl >= AD / 2 - R) {
-            const int pr0 = (cl - (AD / 2 - R)) >> 1;
+          const int cl0 = dt * 32 + gq * 8;  // channel within this wave's half: cl0 + 4 half
+          if (R > 0 && kh == 1 && cl0 >= AD / 2 - R) {
+            const int pr0 = (cl0 - (AD / 2 - R)) >> 1;  // pair: pr0 + 2 half + i2/2
 #pragma unroll
             for (int i2 = 0; i2 < 4; i2 += 2) {
+              const double f0 = invf[pr0 + i2 / 2], f1 = invf[pr0 + 2 + i2 / 2];
               float c, sn;
-              rope_pair(pos, a.inv_freq[pr0 + i2 / 2], c, sn);
+              rope_pair(pos, half ? f1 : f0, c, sn);
               const float xv = v[i2], yv = v[i2 + 1];
               v[i2] = xv * c - yv * sn;
               v[i2 + 1] = xv * sn + yv * c;
@@ -523,13 +554,14 @@ attend_mfma_kernel(AttendArgs a) {
         val[2] = s0[1];
         val[3] = s1[1];
         // lanes >= 32 write group 2gp + 1: their half * 8 channels are part of ovoff
-        __builtin_amdgcn_raw_buffer_store_b128(val, o_rs, ovoff + (dt * 32 + 2 * gp * 8) * 2, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128(val, o_rs, ovoff + (dt * 32 + 2 * gp * 8) * 2, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // one group at a time: keeps the epilogue's registers few
       }
     }
   };
 
   for (int s = -1;; ++s) {
-    __syncthreads();  // X(s): P(s) and the rescale factor are published
+    lds_barrier();  // X(s): P(s) and the rescale factor are published
     const bool has = s >= 0 && jp < n_mine;  // this step accumulates tile s
     const unsigned char* tb = lds + ((s + NSLOT) % NSLOT) * ATILE;
     if (has) {
@@ -540,6 +572,8 @@ attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
       }
+#pragma unroll
+      for (int i = 0; i < VPF; ++i) vr[i] = vfrag(tb, i);
       const int par = s & 1;
       pb[0] = pbuf[((par * 2 + hb) * 2 + 0) * 64 + lane];
       pb[1] = pbuf[((par * 2 + hb) * 2 + 1) * 64 + lane];
@@ -550,12 +584,12 @@ attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
       }
-      pv_half(tb, 0);
+      pv_steps(tb, 0);
     }
-    __syncthreads();  // Y(s)
+    lds_barrier();  // Y(s)
     if (s < 0) continue;
     if (!has) break;
-    pv_half(tb, 1);
+    pv_steps(tb, NDT);
     if (tp + 1 == cp.n_tiles) {
       finish(cp, 1.f / lsum[(s & 1) * 64 + head]);
       tp = 0;
