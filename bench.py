@@ -315,12 +315,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA / decode workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["csa_prefill", "hca_prefill", "csa_decode"], default=None,
+                    help="run one workload alone (for profiling); prints its figures only")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="launch one device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path would shard by query ranges, see DESIGN.md", file=sys.stderr)
+              "the path would shard by query ranges (one all-gather of the pooled K=V)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -334,7 +336,15 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written")
         del src, dst
+    if args.only in ("hca_prefill", "csa_decode"):
+        fn = run_hca_prefill if args.only == "hca_prefill" else run_decode
+        print(json.dumps({"only": args.only, **fn(torch, args.steps, args.warmup)}), flush=True)
+        return
     w, wall, kern = run_csa_prefill(torch, args.steps, args.warmup)
+    if args.only == "csa_prefill":
+        print(json.dumps({"only": args.only, "query_tokens_per_s": w.S / wall,
+                          "ms_per_step": wall * 1e3, "kernels": kern}), flush=True)
+        return
     extra = {}
     if not args.no_extra:
         extra["hca_prefill"] = run_hca_prefill(torch, max(3, args.steps // 4), 1)
