@@ -6,8 +6,10 @@ rope 64, m=4, 64 x 128 indexer, top-512, window 128, bf16).  One step = the whol
 path over one batch: csa_compress (K=V pool) + csa_compress (indexer keys) + csa_index_topk +
 swa_concat + csa_attend, inputs resident in HBM.
 
-Also reported in the same line ("workloads"): HCA prefill query-tokens/s at S=65536 and CSA
-decode us/step for 64 sequences of 16K-128K context, plus per-kernel times and roofline
+Also reported in the same line ("workloads"): HCA prefill query-tokens/s at S=65536, CSA
+decode us/step for 64 sequences of 16K-128K context, and the mixed eight-layer stack
+(sliding, sliding, CSA, HCA, CSA, HCA, CSA, HCA) at S=32768 prefilled in 4096-query chunks,
+plus per-kernel times and roofline
 fractions.  "roofline" is for the dominant kernel (csa_attend): algorithmic flops per launch
 over the launch's average duration (HIP events on the launch stream).  "cpu_baseline" is the
 fp64 CPU oracle timed on this host's cores over a bounded sample of the same workload.
@@ -266,6 +268,78 @@ def run_decode(torch, steps, warmup):
             "hbm_frac_whole_step": (idx_bytes + att_bytes) / wall / PEAK_HBM}
 
 
+def run_stack(torch, steps, warmup):
+    """The mixed eight-layer stack at S=32768, prefilled in 4096-query chunks (chunk-major).
+
+    Inputs are generated on the device (torch's Philox generator, seeded per layer and tensor,
+    N(0,1) rounded to bf16; fp32 biases, sinks and indexer weights), the same distribution as
+    the keyed host generator the parity tests use: regenerating 17 GB of activations on the
+    host would dominate the run."""
+    import workloads as W
+    from long_context_sparse_09_amd import layers
+
+    w = W.workload(5)
+    S, kinds = w.S, list(w.layer_types)
+    log(f"[bench] stack {kinds} S={S} chunk={w.chunk}: generating inputs on the device")
+    sh = layers.LayerShape(w.B, S, w.H, w.D, w.r, w.m, w.m_hca, w.nI, w.cI, w.k, w.W, w.base,
+                           torch.bfloat16)
+    shapes = {"q": (w.H, w.D), "kv": (w.D,), "gate": (w.D,), "q_idx": (w.nI, w.cI),
+              "k_idx": (w.cI,), "g_idx": (w.cI,)}
+    need = {"sliding": ("q", "kv"), "hca": ("q", "kv", "gate"), "csa": tuple(shapes)}
+    inps, bufs = [], []
+    for ell, kind in enumerate(kinds):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed * 1000 + ell)
+        d = {n: torch.randn((1, S) + shapes[n], generator=g, device="cuda",
+                            dtype=torch.float32).to(torch.bfloat16) for n in need[kind]}
+        d["w_idx"] = torch.randn((1, S, w.nI), generator=g, device="cuda")
+        d["sink"] = torch.randn((w.H,), generator=g, device="cuda")
+        d["bias"] = torch.randn((2 * w.m, w.D), generator=g, device="cuda")
+        d["bias_idx"] = torch.randn((2 * w.m, w.cI), generator=g, device="cuda")
+        d["bias_hca"] = torch.randn((w.m_hca, w.D), generator=g, device="cuda")
+        inps.append(d)
+        bufs.append(layers.LayerBuffers(sh, kinds=(kind,)))
+    torch.cuda.synchronize()
+
+    def step():
+        layers.stack_prefill_chunked(kinds, inps, bufs, w.chunk)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] stack: timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    # one step with events around each layer's chunk loop, per layer type
+    per_kind = {}
+    for ell, kind in enumerate(kinds):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        layers.prefill_chunked(kind, inps[ell], bufs[ell], w.chunk)
+        ev1.record()
+        per_kind.setdefault(kind, []).append((ev0, ev1))
+    torch.cuda.synchronize()
+    layer_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in per_kind.items()}
+    win, sel = csa_keys_per_query(S, w.W, w.m, w.k)
+    t = np.arange(S, dtype=np.int64)
+    hkeys = np.minimum(t + 1, w.W) + (t + 1) // w.m_hca
+    fl = {"csa": attend_flops((win + sel).sum(), w.H, w.D) + index_flops(S, w.m, w.nI, w.cI),
+          "hca": attend_flops(hkeys.sum(), w.H, w.D),
+          "sliding": attend_flops(win.sum(), w.H, w.D)}
+    total = sum(fl[k] for k in kinds)
+    del inps, bufs
+    return {"workload": w.name, "layer_types": kinds, "chunk": w.chunk,
+            "query_tokens_per_s": S / wall, "ms_per_step": wall * 1e3,
+            "layer_ms": layer_ms,
+            "alg_flops_per_step": total, "TFLOP/s": total / wall / 1e12,
+            "mfma_frac_whole_step": total / wall / PEAK_BF16,
+            "inputs": "device-generated N(0,1), torch Philox, seeded per layer"}
+
+
 # ----------------------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(n_sample=640):
@@ -315,7 +389,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA / decode workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["csa_prefill", "hca_prefill", "csa_decode"], default=None,
+    ap.add_argument("--only", choices=["csa_prefill", "hca_prefill", "csa_decode", "stack"], default=None,
                     help="run one workload alone (for profiling); prints its figures only")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="launch one device copy of this size first (counter calibration)")
@@ -336,8 +410,9 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written")
         del src, dst
-    if args.only in ("hca_prefill", "csa_decode"):
-        fn = run_hca_prefill if args.only == "hca_prefill" else run_decode
+    if args.only in ("hca_prefill", "csa_decode", "stack"):
+        fn = {"hca_prefill": run_hca_prefill, "csa_decode": run_decode,
+              "stack": run_stack}[args.only]
         print(json.dumps({"only": args.only, **fn(torch, args.steps, args.warmup)}), flush=True)
         return
     w, wall, kern = run_csa_prefill(torch, args.steps, args.warmup)
@@ -350,6 +425,8 @@ def main():
         extra["hca_prefill"] = run_hca_prefill(torch, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
         extra["csa_decode"] = run_decode(torch, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        extra["stack8_prefill"] = run_stack(torch, max(2, args.steps // 5), 1)
         torch.cuda.empty_cache()
     att = kern["csa_attend"]
     src = kernel_hash("attend_mfma.hip", "common.h")

@@ -105,6 +105,85 @@ def sliding_layer(inp: Dict[str, torch.Tensor], buf: LayerBuffers, rope_pos_offs
     return buf.out
 
 
+def prefill_chunk(kind: str, inp: Dict[str, torch.Tensor], buf: LayerBuffers, c0: int, c1: int,
+                  p0: torch.Tensor, rope_pos_offset: int = 0, stream=None) -> None:
+    """Queries [c0, c1) of one layer's prefill (B = 1), with every earlier key visible.
+
+    The chunk pools the entries its tokens close (entries [c0//m, c1//m); an overlapping CSA
+    entry also reads the m tokens before its window, which earlier chunks hold), rotates its
+    own window rows into kv_win (rows of earlier chunks are already there: the window halo),
+    then scores and attends its queries.  p0 is a device int32 [1] holding c0.  Entries and
+    window rows past the chunk are never visible to its queries, whatever they hold."""
+    sh = buf.sh
+    if sh.B != 1:
+        raise ValueError("chunked prefill runs one sequence (B = 1)")
+    q = inp["q"][:, c0:c1]
+    out = buf.out[:, c0:c1]
+    z = buf.zeros_b
+    if kind == "csa":
+        e0, e1 = c0 // sh.m, c1 // sh.m
+        if e1 > e0:
+            csa_compress(inp["kv"], inp["gate"], inp["bias"], buf.pool, sh.m, True, e0, e1,
+                         rope_dim=sh.r, rope_theta=sh.base, rope_pos_offset=rope_pos_offset,
+                         stream=stream)
+            csa_compress(inp["k_idx"], inp["g_idx"], inp["bias_idx"], buf.k_pool, sh.m, True,
+                         e0, e1, rope_dim=0, stream=stream)
+        csa_index_topk(inp["q_idx"][:, c0:c1], inp["w_idx"][:, c0:c1], buf.k_pool, p0,
+                       buf.n_pool, buf.topk_idx[:, c0:c1], None, sh.m, buf.workspace,
+                       stream=stream)
+    elif kind == "hca":
+        e0, e1 = c0 // sh.m_hca, c1 // sh.m_hca
+        if e1 > e0:
+            csa_compress(inp["kv"], inp["gate"], inp["bias_hca"], buf.pool_h, sh.m_hca, False,
+                         e0, e1, rope_dim=sh.r, rope_theta=sh.base,
+                         rope_pos_offset=rope_pos_offset, stream=stream)
+    elif kind != "sliding":
+        raise ValueError(f"layer kind {kind!r}")
+    swa_concat(inp["kv"][:, c0:c1], buf.kv_win, z, p0, sh.r, sh.base, rope_pos_offset,
+               stream=stream)
+    if kind == "csa":
+        csa_attend(q, buf.kv_win, z, buf.pool, buf.topk_idx[:, c0:c1], inp["sink"], p0, out,
+                   sh.W, sh.r, sh.base, rope_pos_offset, stream=stream)
+    else:
+        has_pool = kind == "hca" and buf.Nh > 0
+        hca_attend(q, buf.kv_win, z, buf.pool_h if has_pool else None,
+                   buf.n_pool_h if has_pool else None, sh.m_hca, inp["sink"], p0, out, sh.W,
+                   sh.r, sh.base, rope_pos_offset, stream=stream)
+
+
+def chunk_starts(S: int, chunk: int, device) -> torch.Tensor:
+    """Device int32 start positions of the query chunks of one sequence of S tokens."""
+    if chunk <= 0:
+        raise ValueError("chunk must be positive")
+    return torch.arange(0, S, chunk, dtype=torch.int32, device=device)
+
+
+def prefill_chunked(kind: str, inp: Dict[str, torch.Tensor], buf: LayerBuffers, chunk: int,
+                    rope_pos_offset: int = 0, stream=None) -> torch.Tensor:
+    """One layer's prefill in query chunks of `chunk` tokens; same result as the one-shot layer."""
+    S = buf.sh.S
+    starts = chunk_starts(S, chunk, buf.kv_win.device)
+    for i, c0 in enumerate(range(0, S, chunk)):
+        prefill_chunk(kind, inp, buf, c0, min(S, c0 + chunk), starts[i:i + 1], rope_pos_offset,
+                      stream)
+    return buf.out
+
+
+def stack_prefill_chunked(kinds, inps, bufs, chunk: int, stream=None):
+    """A stack of layers prefilled chunk by chunk: every layer takes chunk c before any layer
+    takes chunk c+1, the order a serving engine follows when each layer feeds the next.  The
+    layers here have their own inputs (no projections between them), so the order changes
+    no result."""
+    if not (len(kinds) == len(inps) == len(bufs)):
+        raise ValueError("one input set and one buffer set per layer")
+    S = bufs[0].sh.S
+    starts = chunk_starts(S, chunk, bufs[0].kv_win.device)
+    for i, c0 in enumerate(range(0, S, chunk)):
+        for kind, inp, buf in zip(kinds, inps, bufs):
+            prefill_chunk(kind, inp, buf, c0, min(S, c0 + chunk), starts[i:i + 1], stream=stream)
+    return [b.out for b in bufs]
+
+
 def to_device(arrays: Dict, device="cuda") -> Dict[str, torch.Tensor]:
     """Storage-encoded numpy arrays (uint16 = bf16 bits, float32, int) -> device tensors."""
     import numpy as np

@@ -1,0 +1,144 @@
+"""Chunked prefill and the mixed eight-layer stack (S=32768, 4096-query chunks) on the GPU.
+
+Chunked prefill: queries of chunk [c0, c1) see every earlier key, so a layer prefilled chunk
+by chunk must give the one-shot layer's result.  Where the chunk length is a multiple of the
+kernels' query tiles the arithmetic per output element is the same, so the comparison is
+bit-exact (outputs, top-k lists); a ragged chunk length is held to the bf16 tolerance against
+the one-shot layer and the top-k lists must still be identical.
+
+The full-size stack runs whole on the GPU in the benchmark's chunk order; the CPU oracle
+recomputes sampled queries (chunk edges included) of one layer of each type.  Tolerance:
+|d| <= 2e-2 * max|ref| over the sampled rows; top-k lists exact except inside the 1e-4
+relative band of the k-th score.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import assert_close, check_topk_row, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from long_context_sparse_09_amd import layers  # noqa: E402
+
+R = oracle.round_bf16
+W5 = W.workload(5)
+NAMES = {"sliding": ["q", "kv"], "hca": ["q", "kv", "gate"], "csa": None}
+
+
+def _shape(w, S):
+    return layers.LayerShape(w.B, S, w.H, w.D, w.r, w.m, w.m_hca, w.nI, w.cI, w.k, w.W, w.base,
+                             torch.bfloat16)
+
+
+def _oneshot(kind, d, buf):
+    if kind == "csa":
+        return layers.csa_layer(d, buf)
+    if kind == "hca":
+        return layers.hca_layer(d, buf)
+    return layers.sliding_layer(d, buf)
+
+
+def _layer_of(kind):
+    return {"sliding": 0, "csa": 2, "hca": 3}[kind]
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "sliding"])
+@pytest.mark.parametrize("S,chunk,exact", [(4096, 1024, True), (2000, 333, False)])
+def test_chunked_matches_oneshot(kind, S, chunk, exact):
+    print(f"[stack] chunked {kind} S={S} chunk={chunk}", flush=True)
+    w = W.scaled(W5, S=S)
+    d = layers.to_device(W.layer_inputs(w, _layer_of(kind), names=NAMES[kind]))
+    a = layers.LayerBuffers(_shape(w, S), kinds=(kind,))
+    b = layers.LayerBuffers(_shape(w, S), kinds=(kind,))
+    ref = host(_oneshot(kind, d, a))
+    got = host(layers.prefill_chunked(kind, d, b, chunk))
+    torch.cuda.synchronize()
+    if kind == "csa":
+        ia, ib = a.topk_idx.cpu().numpy(), b.topk_idx.cpu().numpy()
+        assert np.array_equal(ia, ib), f"top-k lists differ at {np.argwhere(ia != ib)[:4]}"
+        assert np.array_equal(host(a.pool), host(b.pool))
+        assert np.array_equal(host(a.k_pool), host(b.k_pool))
+    if kind == "hca":
+        assert np.array_equal(host(a.pool_h), host(b.pool_h))
+    assert np.array_equal(host(a.kv_win), host(b.kv_win))
+    if exact:
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{kind}: {len(bad)} elements differ, first at {bad[:3]}"
+    else:
+        assert_close(got, ref, "bf16", f"chunked {kind} S={S} chunk={chunk}")
+
+
+def test_stack_chunk_order_matches_per_layer():
+    """Chunk-major order over a small mixed stack equals each layer prefilled on its own."""
+    print("[stack] chunk-major order, 4 layers S=2048 chunk 512", flush=True)
+    w = W.scaled(W5, S=2048)
+    kinds = ["sliding", "csa", "hca", "csa"]
+    inps, bufs, refs = [], [], []
+    for ell, kind in enumerate(kinds):
+        d = layers.to_device(W.layer_inputs(w, ell))
+        inps.append(d)
+        bufs.append(layers.LayerBuffers(_shape(w, w.S), kinds=(kind,)))
+        one = layers.LayerBuffers(_shape(w, w.S), kinds=(kind,))
+        refs.append(host(layers.prefill_chunked(kind, d, one, 512)))
+    outs = layers.stack_prefill_chunked(kinds, inps, bufs, 512)
+    for ell, (o, r) in enumerate(zip(outs, refs)):
+        assert np.array_equal(host(o), r), f"layer {ell} ({kinds[ell]}) differs"
+
+
+SAMPLE = [0, 1, 127, 128, 4095, 4096, 4097, 8191, 8192, 20000, 32766, 32767]
+
+
+def _window(kv64, t, w):
+    lo = max(0, t - w.W + 1)
+    return oracle.swa_concat(kv64[:, lo:t + 1], [lo], w.r, w.base), lo
+
+
+@pytest.mark.parametrize("kind", ["sliding", "csa", "hca"])
+def test_stack_layer_full_S32768_chunked_sampled(kind):
+    """One layer of each type of the S=32768 stack, prefilled in 4096-query chunks."""
+    w = W5
+    ell = _layer_of(kind)
+    assert w.layer_types[ell] == kind
+    print(f"[stack] layer {ell} ({kind}) S={w.S} chunk={w.chunk}", flush=True)
+    inp = W.layer_inputs(w, ell, names=NAMES[kind])
+    buf = layers.LayerBuffers(_shape(w, w.S), kinds=(kind,))
+    out = layers.prefill_chunked(kind, layers.to_device(inp), buf, w.chunk)
+    torch.cuda.synchronize()
+    kv = W.to_f64(inp["kv"])
+    if kind == "csa":
+        gpu_idx = buf.topk_idx.cpu().numpy()
+        pool = R(oracle.csa_compress(kv, W.to_f64(inp["gate"]), inp["bias"], w.m, True, w.r,
+                                     w.base))
+        k_pool = R(oracle.csa_compress(W.to_f64(inp["k_idx"]), W.to_f64(inp["g_idx"]),
+                                       inp["bias_idx"], w.m, True, 0))
+    elif kind == "hca":
+        pool = R(oracle.csa_compress(kv, W.to_f64(inp["gate"]), inp["bias_hca"], w.m_hca, False,
+                                     w.r, w.base))
+    refs, gots = [], []
+    for t in SAMPLE:
+        win, lo = _window(kv, t, w)
+        q = W.to_f64(W.activation_rows(w, ell, "q", [t]))
+        if kind == "csa":
+            N = pool.shape[1]
+            qi = W.to_f64(W.activation_rows(w, ell, "q_idx", [t]))
+            wi = W.activation_rows(w, ell, "w_idx", [t])
+            s = oracle.index_scores(qi[0], wi[0], k_pool[0, :oracle.n_visible(t, w.m, N)])
+            check_topk_row(gpu_idx[0, t], s, gpu_idx.shape[2], f"t={t}")
+            idx, _ = oracle.csa_index_topk(qi[None], wi[None], k_pool, [t], [N], w.m, w.k)
+            ref = oracle.csa_attend(q[None], R(win), [lo], pool, idx, inp["sink"], [t], w.W, w.r,
+                                    w.base)
+        elif kind == "hca":
+            ref = oracle.hca_attend(q[None], R(win), [lo], pool, [pool.shape[1]], w.m_hca,
+                                    inp["sink"], [t], w.W, w.r, w.base)
+        else:
+            ref = oracle.hca_attend(q[None], R(win), [lo], None, [0], w.m_hca, inp["sink"], [t],
+                                    w.W, w.r, w.base)
+        refs.append(ref[0, 0])
+        gots.append(host(out[0, t]))
+    assert_close(np.stack(gots), np.stack(refs), "bf16", f"stack layer {ell} ({kind}) sampled")
