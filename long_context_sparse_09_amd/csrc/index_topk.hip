@@ -21,7 +21,6 @@ namespace {
 constexpr int IX_NI = 64;     // indexer heads covered by the MFMA path
 constexpr int IX_CI = 128;    // indexer head dim covered by the MFMA path
 constexpr int IX_TILE = 128;  // pool entries per LDS tile (4 sub-tiles of 32)
-constexpr int IX_PITCH = IX_CI * 2 + 16;  // LDS bytes per entry row (16 B pad spreads banks)
 
 __device__ __forceinline__ int visible_entries(const int* q_pos0, const int* n_pool, int b, int t,
                                                int m, int N_cap) {
@@ -33,118 +32,217 @@ __device__ __forceinline__ int visible_entries(const int* q_pos0, const int* n_p
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+constexpr int IX_ROW = IX_CI * 2;  // bytes per indexer key row
+
+// Raw buffer descriptor over [base, base + bytes): reads past the end return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ rsrc_t make_rs(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// Sum of a value across the two 32-lane halves of the wave.
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // MFMA scoring (bf16, 64 heads x 128 dims).  S = Q . K^T per query on
 // v_mfma_f32_32x32x16_bf16: A = Q (32 heads x 16 dims, registers), B = K^T (16 dims x 32
-// entries, LDS).  The C tile holds 16 heads of one entry per lane, so the ReLU-weighted head
-// sum is 16 local FMAs and one cross-half shuffle.
+// entries).  The C tile holds 16 heads of one entry per lane, so the ReLU-weighted head sum
+// is 16 local FMAs and one cross-half shuffle.
 //
-// SPLIT = false (prefill): a block owns 4*QPW consecutive queries (QPW per wave); all waves
-//   walk the same 128-entry tiles, so each LDS tile is reused by every query of the block.
-// SPLIT = true (decode, one query per block): the block owns a chunk of tiles; wave w scores
-//   sub-tile w of every tile.
+// Prefill (index_score_mfma): a block owns NWV consecutive queries, one per wave, two waves
+// per SIMD (so one wave's ReLU-weighted head sums overlap the other's MFMAs); all waves walk
+// the same 128-entry LDS tiles, so each tile is reused by every query of the block.
 // ---------------------------------------------------------------------------
-template <int QPW, bool SPLIT>
-__global__ void __launch_bounds__(256, 1) index_score_mfma(
+template <int NWV>
+__global__ void __launch_bounds__(512, 1) index_score_mfma(
     const bf16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const bf16_t* __restrict__ k_pool, const int* __restrict__ q_pos0,
-    const int* __restrict__ n_pool, float* __restrict__ scores, int T, int N_cap, int m,
-    int tiles_per_chunk) {
-  __shared__ __attribute__((aligned(16))) unsigned char ktile[IX_TILE * IX_PITCH];
+    const int* __restrict__ n_pool, float* __restrict__ scores, int T, int N_cap, int m) {
+  // two tile slots: tile s+1 streams into one (LDS-DMA) while tile s is read from the other
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][IX_TILE * IX_ROW];
+  static_assert(NWV == 8, "launch bounds are written for 8 waves");
+  constexpr int LPW = 4;  // LDS-DMA instructions (1 KB each) per wave per tile
+  static_assert(LPW * NWV * 1024 == IX_TILE * IX_ROW, "waves x instructions cover a tile");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int b = blockIdx.z;
-  constexpr int QB = SPLIT ? 1 : 4 * QPW;
-  // heaviest (latest) query blocks first
-  const int t0 = SPLIT ? blockIdx.x : (gridDim.x - 1 - blockIdx.x) * QB;
-
-  int tq[QPW], V[QPW];
-#pragma unroll
-  for (int qi = 0; qi < QPW; ++qi) {
-    tq[qi] = SPLIT ? t0 : t0 + wave * QPW + qi;
-    V[qi] = tq[qi] < T ? visible_entries(q_pos0, n_pool, b, tq[qi], m, N_cap) : 0;
-  }
-  const int t_last = min(t0 + QB - 1, T - 1);
+  // heaviest (latest) query blocks first; wave w scores query t0 + w
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * NWV;
+  const int tq = t0 + wave;
+  const int V = tq < T ? visible_entries(q_pos0, n_pool, b, tq, m, N_cap) : 0;
+  const int t_last = min(t0 + NWV - 1, T - 1);
   const int Vmax = visible_entries(q_pos0, n_pool, b, t_last, m, N_cap);
   const int n_tiles = (Vmax + IX_TILE - 1) / IX_TILE;
-  int tile_begin = 0, tile_end = n_tiles;
-  if (SPLIT) {
-    tile_begin = blockIdx.y * tiles_per_chunk;
-    tile_end = min(n_tiles, tile_begin + tiles_per_chunk);
-  }
-  if (tile_begin >= tile_end) return;  // block-uniform
+  if (n_tiles == 0) return;  // block-uniform
 
-  // Q fragments and head weights of this wave's queries
-  bf16x8_t qa[QPW][2][IX_CI / 16];
-  float wv[QPW][2][16];
+  // Tile loads: LDS chunk p (16 bytes) of a slot holds chunk c = (p & 15) ^ (row & 15) of entry
+  // row = p >> 4, so the B-operand reads (32 rows, one chunk column) hit 16 distinct bank
+  // groups.  Wave w fills chunks 64*LPW*w .. (LPW instructions of 64 lanes).  Rows past N_cap
+  // lie beyond the buffer descriptor and read as zeros.
+  const rsrc_t krs = make_rs(k_pool + static_cast<size_t>(b) * N_cap * IX_CI,
+                             static_cast<unsigned>(N_cap) * IX_ROW);
+  unsigned soff[LPW];
 #pragma unroll
-  for (int qi = 0; qi < QPW; ++qi) {
-    const int t = min(tq[qi], T - 1);
-    const size_t qrow = static_cast<size_t>(b) * T + t;
+  for (int j = 0; j < LPW; ++j) {
+    const int p = (wave * LPW + j) * 64 + lane;
+    const int row = p >> 4;
+    soff[j] = static_cast<unsigned>(row * IX_ROW + (((p & 15) ^ (row & 15)) << 4));
+  }
+  auto issue = [&](int tile, int slot) {
+    const unsigned base = static_cast<unsigned>(tile) * (IX_TILE * IX_ROW);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (lds_void*)(&ktile[slot][(wave * LPW + j) * 1024]), 16, soff[j] + base, 0, 0, 0);
+  };
+  issue(0, 0);
+
+  // Q fragments and head weights of this wave's query
+  bf16x8_t qa[2][IX_CI / 16];
+  float wv[2][16];
+  {
+    const size_t qrow = static_cast<size_t>(b) * T + min(tq, T - 1);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const bf16_t* qp = q_idx + (qrow * IX_NI + hb * 32 + l32) * IX_CI + half * 8;
 #pragma unroll
       for (int ks = 0; ks < IX_CI / 16; ++ks)
-        qa[qi][hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + ks * 16));
+        qa[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + ks * 16));
       const float* wp = w_idx + qrow * IX_NI + hb * 32 + half * 4;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) wv[qi][hb][e] = wp[(e >> 2) * 8 + (e & 3)];
+      for (int e = 0; e < 16; ++e) wv[hb][e] = wp[(e >> 2) * 8 + (e & 3)];
     }
   }
+  float* srow = scores + (static_cast<size_t>(b) * T + tq) * N_cap;
+  const int rsw = l32 & 15;  // B-operand chunk swizzle of this lane's row
 
-  const bf16_t* kbase = k_pool + static_cast<size_t>(b) * N_cap * IX_CI;
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int n0 = tile * IX_TILE;
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int pass = 0; pass < IX_TILE * IX_CI * 2 / (256 * 16); ++pass) {
-      const int row = pass * 16 + (threadIdx.x >> 4);
-      const int ch = threadIdx.x & 15;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n0 + row < N_cap)
-        v = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(n0 + row) * IX_CI + ch * 8);
-      *reinterpret_cast<uint4*>(ktile + row * IX_PITCH + ch * 16) = v;
-    }
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    // this wave's part of tile `tile` has landed (and its earlier score stores are done);
+    // after the barrier every part has, and every wave is past tile-1, whose slot is reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    if (tile + 1 < n_tiles) issue(tile + 1, (tile + 1) & 1);
+    const unsigned char* kt = ktile[tile & 1];
+    const int n0 = tile * IX_TILE;
+    if (n0 >= V) continue;  // wave-uniform: this query sees none of the tile
 
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      if (SPLIT && sub != wave) continue;
-      f32x16_t acc[QPW][2];
+      f32x16_t acc[2];
 #pragma unroll
-      for (int qi = 0; qi < QPW; ++qi)
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[hb][e] = 0.f;
+      // all B fragments of the sub-tile first: the LDS latency overlaps the MFMAs
+      const unsigned char* brow = kt + (sub * 32 + l32) * IX_ROW;
+      bf16x8_t bk[IX_CI / 16];
+#pragma unroll
+      for (int ks = 0; ks < IX_CI / 16; ++ks)
+        bk[ks] = *reinterpret_cast<const bf16x8_t*>(brow + (((2 * ks + half) ^ rsw) << 4));
+#pragma unroll
+      for (int ks = 0; ks < IX_CI / 16; ++ks)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
+          acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][ks], bk[ks], acc[hb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 LDS reads ...
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // ... ahead of the 16 MFMAs
+      // ReLU as an integer max: non-negative floats are non-negative integers, and -0 -> +0
+      float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[qi][hb][e] = 0.f;
-      const unsigned char* brow = ktile + (sub * 32 + l32) * IX_PITCH + half * 16;
-#pragma unroll
-      for (int ks = 0; ks < IX_CI / 16; ++ks) {
-        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(brow + ks * 32);
-#pragma unroll
-        for (int qi = 0; qi < QPW; ++qi)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            acc[qi][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qi][hb][ks], bk, acc[qi][hb], 0, 0, 0);
+      for (int e = 0; e < 16; ++e) {
+        p0 += wv[0][e] * __int_as_float(max(__float_as_int(acc[0][e]), 0));
+        p1 += wv[1][e] * __int_as_float(max(__float_as_int(acc[1][e]), 0));
       }
+      const float part = xhalf_sum(p0 + p1);
       const int n = n0 + sub * 32 + l32;
-#pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) {
-        float part = 0.f;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) part += wv[qi][hb][e] * fmaxf(acc[qi][hb][e], 0.f);
-        part += __shfl_xor(part, 32);
-        if (half == 0 && n < V[qi])
-          scores[(static_cast<size_t>(b) * T + tq[qi]) * N_cap + n] = part;
-      }
+      if (half == 0 && n < V) srow[n] = part;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-sized T (index_score_stream): the scan is bound by reading the indexer keys once
+// (64 flops per byte), so every wave streams its own EPW consecutive entries of one query
+// straight from HBM into B-operand registers, one 32-entry sub-tile ahead of the MFMAs.  No
+// LDS, no barriers: waves are independent and many are resident, which keeps enough key
+// bytes in flight to cover HBM latency.  Lane (l32, half) loads 16 bytes of entry row l32 per
+// 16-dim step; the 8 steps of a sub-tile together read whole 256-byte rows.
+// ---------------------------------------------------------------------------
+template <int EPW>
+__global__ void __launch_bounds__(256) index_score_stream(
+    const bf16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const bf16_t* __restrict__ k_pool, const int* __restrict__ q_pos0,
+    const int* __restrict__ n_pool, float* __restrict__ scores, int T, int N_cap, int m) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int t = blockIdx.y, b = blockIdx.z;
+  const int V = visible_entries(q_pos0, n_pool, b, t, m, N_cap);
+  const int e0 = (blockIdx.x * 4 + wave) * EPW;
+  if (e0 >= V) return;  // wave-uniform
+  const int e1 = min(V, e0 + EPW);
+  const size_t qrow = static_cast<size_t>(b) * T + t;
+
+  bf16x8_t qa[2][IX_CI / 16];
+  float wv[2][16];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const bf16_t* qp = q_idx + (qrow * IX_NI + hb * 32 + l32) * IX_CI + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < IX_CI / 16; ++ks)
+      qa[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + ks * 16));
+    const float* wp = w_idx + qrow * IX_NI + hb * 32 + half * 4;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) wv[hb][e] = wp[(e >> 2) * 8 + (e & 3)];
+  }
+
+  // rows past e1 are clamped to e1 - 1 (a visible row): loads stay in bounds, results unused
+  const bf16_t* kb = k_pool + static_cast<size_t>(b) * N_cap * IX_CI + half * 8;
+  uint4 cur[IX_CI / 16], nxt[IX_CI / 16];
+  {
+    const bf16_t* kr = kb + static_cast<size_t>(min(e0 + l32, e1 - 1)) * IX_CI;
+#pragma unroll
+    for (int ks = 0; ks < IX_CI / 16; ++ks) cur[ks] = *reinterpret_cast<const uint4*>(kr + ks * 16);
+  }
+  float* srow = scores + qrow * N_cap;
+  for (int n0 = e0; n0 < e1; n0 += 32) {
+    if (n0 + 32 < e1) {  // wave-uniform
+      const bf16_t* kr = kb + static_cast<size_t>(min(n0 + 32 + l32, e1 - 1)) * IX_CI;
+#pragma unroll
+      for (int ks = 0; ks < IX_CI / 16; ++ks) nxt[ks] = *reinterpret_cast<const uint4*>(kr + ks * 16);
+    }
+    f32x16_t acc[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[hb][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < IX_CI / 16; ++ks) {
+      const bf16x8_t bk = as_bf16x8(cur[ks]);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][ks], bk, acc[hb], 0, 0, 0);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) part += wv[hb][e] * fmaxf(acc[hb][e], 0.f);
+    part = xhalf_sum(part);
+    const int n = n0 + l32;
+    if (half == 0 && n < e1) srow[n] = part;
+#pragma unroll
+    for (int ks = 0; ks < IX_CI / 16; ++ks) cur[ks] = nxt[ks];
   }
 }
 
@@ -186,17 +284,16 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
     const bf16_t* qp = static_cast<const bf16_t*>(q_idx);
     const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
     if (T >= 8) {
-      constexpr int QPW = 2;
-      dim3 grid(div_up(T, 4 * QPW), 1, B);
-      hipLaunchKernelGGL((index_score_mfma<QPW, false>), grid, dim3(256), 0, st, qp, w_idx, kp,
-                         q_pos0, n_pool, scores, T, N_cap, m, 0);
+      constexpr int NWV = 8;  // queries per block, one per wave, two waves per SIMD
+      dim3 grid(div_up(T, NWV), 1, B);
+      hipLaunchKernelGGL((index_score_mfma<NWV>), grid, dim3(NWV * 64), 0, st, qp, w_idx, kp,
+                         q_pos0, n_pool, scores, T, N_cap, m);
     } else {
-      // one query per block, entry tiles split over blocks (decode-sized T)
-      const int tiles = (N_cap + IX_TILE - 1) / IX_TILE;
-      const int tpc = 8;  // 1024 entries per block
-      dim3 grid(T, div_up(tiles, tpc), B);
-      hipLaunchKernelGGL((index_score_mfma<1, true>), grid, dim3(256), 0, st, qp, w_idx, kp,
-                         q_pos0, n_pool, scores, T, N_cap, m, tpc);
+      // decode-sized T: one query per block row, 4 waves x EPW entries per block
+      constexpr int EPW = 256;
+      dim3 grid(div_up(N_cap, 4 * EPW), T, B);
+      hipLaunchKernelGGL((index_score_stream<EPW>), grid, dim3(256), 0, st, qp, w_idx, kp, q_pos0,
+                         n_pool, scores, T, N_cap, m);
     }
     return hipGetLastError();
   }
@@ -213,107 +310,376 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: radix select on order-preserving uint32 keys (4 passes of 8 bits, per-wave LDS
-// histograms, block suffix scan to find each digit), then an index-ordered compaction that
-// takes every key above the threshold and the lowest-index keys equal to it.
+// Top-k of one query row (one block per row).
+//
+// Keys: order-preserving uint32 images of the fp32 scores (-0 ranked as +0).  Thread tid
+// owns indices j*NT + tid; the first KPT of them stay in registers, later ones are re-read
+// (coalesced) from the score row on every pass.
+//
+// Threshold: radix select over 8 passes of 4-bit digits, most significant first.  Each
+// lane counts into its own column of a per-wave [16 digits][64 lanes] LDS histogram, so the
+// increments never collide whatever the score distribution (a shared 256-bin histogram
+// serialises when most keys share a digit, as the top byte of similar-magnitude floats
+// does).  The pass stops early once the chosen digit's bucket holds exactly the keys still
+// needed.
+//
+// Output: index-ordered compaction through LDS bitmaps, segment by segment (32768 indices):
+// one bit per key above the threshold and one per key equal to it (both from wave ballots),
+// a block scan of the equal-key popcounts keeps the lowest-index equal keys that are needed
+// (ties to the lower entry index), and a block scan of the selected popcounts gives every
+// word its output offset.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u << 1) == 0) u = 0;  // -0.0 ranks as +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return max(u, 1u);  // 0 marks "no key" (only one negative NaN pattern is moved, to 1)
 }
 
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Block-wide exclusive prefix sum of v over threads in tid order; *total = block sum.
 template <int NT>
-__global__ void __launch_bounds__(NT) topk_kernel(const float* __restrict__ scores,
-                                                  const int* __restrict__ q_pos0,
-                                                  const int* __restrict__ n_pool,
-                                                  int* __restrict__ topk_idx,
-                                                  float* __restrict__ topk_score, int T, int N_cap,
-                                                  int m, int k) {
+__device__ __forceinline__ int block_scan_excl(int v, int* total, int* wsum) {
   constexpr int NW = NT / 64;
-  static_assert(NT >= 256, "one thread per histogram bin");
-  __shared__ uint32_t hist[NW][256];
-  __shared__ int scan_w[NW];
-  __shared__ int wave_tot[NW];
-  __shared__ int sh_digit, sh_above;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = wsum[w];
+    before += (w < wave) ? c : 0;
+    all += c;
+  }
+  __syncthreads();  // wsum reusable
+  *total = all;
+  return before + incl - v;
+}
+
+constexpr int kSegIdx = 32768;          // indices per compaction segment
+constexpr int kSegWords = kSegIdx / 32;  // bitmap words per segment
+
+template <int NT, int KPT>
+__global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ scores,
+                                                 const int* __restrict__ q_pos0,
+                                                 const int* __restrict__ n_pool,
+                                                 int* __restrict__ topk_idx,
+                                                 float* __restrict__ topk_score, int T, int N_cap,
+                                                 int m, int k) {
+  constexpr int NW = NT / 64;
+  static_assert(kSegIdx % NT == 0 && NT % 64 == 0, "segment = whole block strides");
+  static_assert(KPT * NT <= kSegIdx, "register keys must fit the first segment");
+  __shared__ uint32_t hist[NW][16][64];
+  __shared__ uint32_t gtbits[kSegWords], eqbits[kSegWords];
+  __shared__ int tot[16];
+  __shared__ int wsum[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qrow = blockIdx.x;
   const int b = qrow / T, t = qrow % T;
   const int V = visible_entries(q_pos0, n_pool, b, t, m, N_cap);
   const float* s = scores + static_cast<size_t>(qrow) * N_cap;
-  const int kk = min(k, V);
-  const bool take_all = (kk == V);
-  uint32_t prefix = 0, mask = 0;
-  int remaining = kk;
-
-  if (!take_all) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      for (int i = tid; i < NW * 256; i += NT) (&hist[0][0])[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < V; i += NT) {
-        const uint32_t key = score_key(s[i]);
-        if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // suffix sums over the 256 bins: thread j < 256 holds bin d = 255 - j
-      int cnt = 0, incl = 0;
-      if (tid < 256) {
-        const int d = 255 - tid;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) cnt += static_cast<int>(hist[w][d]);
-        incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int v = __shfl_up(incl, off);
-          if (lane >= off) incl += v;
-        }
-        if (lane == 63) scan_w[wave] = incl;
-      }
-      __syncthreads();
-      if (tid < 256) {
-        for (int w = 0; w < wave; ++w) incl += scan_w[w];
-        const int above = incl - cnt;  // keys with a larger digit
-        if (above < remaining && remaining <= incl) { sh_digit = 255 - tid; sh_above = above; }
-      }
-      __syncthreads();
-      const uint32_t d = static_cast<uint32_t>(sh_digit);
-      remaining -= sh_above;
-      prefix |= d << shift;
-      mask |= 255u << shift;
-      __syncthreads();
-    }
-  }
-
-  // index-ordered compaction
   int* out_i = topk_idx + static_cast<size_t>(qrow) * k;
   float* out_s = topk_score ? topk_score + static_cast<size_t>(qrow) * k : nullptr;
-  int out_base = 0, eq_base = 0;
-  for (int base = 0; base < V; base += NT) {
-    const int i = base + tid;
-    const bool valid = i < V;
-    const float sv = valid ? s[i] : 0.f;
-    bool sel;
-    if (take_all) {
-      sel = valid;
-    } else {
-      const uint32_t key = score_key(sv);
-      const bool gt = valid && key > prefix;
-      const bool eq = valid && key == prefix;
-      int eq_tot;
-      const int eq_rank = eq_base + block_excl_count<NT>(eq, &eq_tot, wave_tot);
-      eq_base += eq_tot;
-      sel = gt || (eq && eq_rank < remaining);
+  const int kk = min(k, V);
+
+  if (kk == V) {  // every visible entry, in index order
+    for (int p = tid; p < k; p += NT) {
+      out_i[p] = p < V ? p : -1;
+      if (out_s) out_s[p] = p < V ? s[p] : 0.f;
+    }
+    return;
+  }
+
+  // keys of this thread: index j*NT + tid; 0 for indices >= V (discounted, never selected)
+  const int n_strides = (V + NT - 1) / NT;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = j * NT + tid;
+    key[j] = (j < n_strides && i < V) ? score_key(s[i]) : 0u;
+  }
+
+  const int n_inv = KPT * NT - min(V, KPT * NT);
+  for (int i = tid; i < NW * 16 * 64; i += NT) (&hist[0][0][0])[i] = 0;
+  __syncthreads();
+
+  uint32_t prefix = 0, mask = 0;
+  int remaining = kk;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 28 - 4 * pass;
+    uint32_t* hcol = &hist[wave][0][lane];
+    // branch-free: a key outside the prefix adds 0
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      atomicAdd(hcol + ((key[j] >> shift) & 15u) * 64,
+                static_cast<uint32_t>((key[j] & mask) == prefix));
+    for (int j = KPT; j < n_strides; ++j) {
+      const int i = j * NT + tid;
+      if (i >= V) break;
+      const uint32_t kj = score_key(s[i]);
+      atomicAdd(hcol + ((kj >> shift) & 15u) * 64, static_cast<uint32_t>((kj & mask) == prefix));
+    }
+    __syncthreads();
+    for (int d = wave; d < 16; d += NW) {
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        c += static_cast<int>(hist[w][d][lane]);
+        hist[w][d][lane] = 0;
+      }
+      c = wave_sum(c);
+      // the n_inv empty register slots hold key 0: digit 0 while the prefix is all zeros
+      if (lane == 0) tot[d] = c - ((d == 0 && prefix == 0u) ? n_inv : 0);
+    }
+    __syncthreads();
+    // every thread derives the digit from the 16 totals (no third barrier)
+    int above = 0, digit = 0, in_digit = 0;
+    for (int d = 15; d >= 0; --d) {
+      const int c = tot[d];
+      if (above + c >= remaining) { digit = d; in_digit = c; break; }
+      above += c;
+    }
+    remaining -= above;
+    prefix |= static_cast<uint32_t>(digit) << shift;
+    mask |= 15u << shift;
+    if (in_digit == remaining) break;  // the whole bucket is taken: threshold found
+  }
+
+  // index-ordered compaction; equal keys (under mask) taken lowest index first
+  int eq_base = 0, out_base = 0;
+  for (int seg0 = 0; seg0 < V; seg0 += kSegIdx) {
+    const int seg_end = min(V, seg0 + kSegIdx);
+    const int j0 = seg0 / NT, j1 = (seg_end + NT - 1) / NT;
+    if (seg0 == 0) {  // register keys all lie in the first segment (KPT * NT <= kSegIdx)
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool ok = key[j] != 0u;
+        const uint32_t km = key[j] & mask;
+        const unsigned long long g = __ballot(ok && km > prefix);
+        const unsigned long long e = __ballot(ok && km == prefix);
+        if (lane < 2) {
+          const int w = j * (NT / 32) + wave * 2 + lane;
+          gtbits[w] = static_cast<uint32_t>(lane ? g >> 32 : g);
+          eqbits[w] = static_cast<uint32_t>(lane ? e >> 32 : e);
+        }
+      }
+    }
+    for (int j = max(j0, KPT); j < j1; ++j) {
+      const bool ok = j * NT + tid < V;
+      const uint32_t km = ok ? (score_key(s[j * NT + tid]) & mask) : 0u;
+      const unsigned long long g = __ballot(ok && km > prefix);
+      const unsigned long long e = __ballot(ok && km == prefix);
+      if (lane < 2) {
+        const int w = (j * NT + wave * 64 - seg0) / 32 + lane;
+        gtbits[w] = static_cast<uint32_t>(lane ? g >> 32 : g);
+        eqbits[w] = static_cast<uint32_t>(lane ? e >> 32 : e);
+      }
+    }
+    __syncthreads();
+    // each thread owns WPT consecutive words of the segment
+    constexpr int WPT = kSegWords / NT > 0 ? kSegWords / NT : 1;
+    const int n_words = (seg_end - seg0 + 31) / 32;
+    const int w0 = tid * WPT;
+    int eq_cnt = 0;
+#pragma unroll
+    for (int q = 0; q < WPT; ++q)
+      if (w0 + q < n_words) eq_cnt += __popc(eqbits[w0 + q]);
+    int eq_tot;
+    int eq_pre = eq_base + block_scan_excl<NT>(eq_cnt, &eq_tot, wsum);
+    uint32_t sel[WPT];
+    int sel_cnt = 0;
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      sel[q] = 0;
+      if (w0 + q < n_words) {
+        uint32_t e = eqbits[w0 + q];
+        const int allow = remaining - eq_pre;  // equal keys still to take
+        const int pe = __popc(e);
+        eq_pre += pe;
+        if (allow <= 0) {
+          e = 0;
+        } else {
+          for (int c = pe; c > allow; --c) e &= ~(1u << (31 - __clz(e)));  // drop highest
+        }
+        sel[q] = gtbits[w0 + q] | e;
+        sel_cnt += __popc(sel[q]);
+      }
     }
     int sel_tot;
-    const int pos = out_base + block_excl_count<NT>(sel, &sel_tot, wave_tot);
-    out_base += sel_tot;
-    if (sel && pos < k) {
-      out_i[pos] = i;
-      if (out_s) out_s[pos] = sv;
+    int pos = out_base + block_scan_excl<NT>(sel_cnt, &sel_tot, wsum);
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      uint32_t w = sel[q];
+      while (w) {
+        const int bit = __ffs(w) - 1;
+        w &= w - 1;
+        const int i = seg0 + (w0 + q) * 32 + bit;
+        if (pos < k) {
+          out_i[pos] = i;
+          if (out_s) out_s[pos] = s[i];
+        }
+        ++pos;
+      }
     }
+    eq_base += eq_tot;
+    out_base += sel_tot;
+    // block_scan_excl ends with a barrier: the bitmaps may be rebuilt for the next segment
   }
   for (int p = kk + tid; p < k; p += NT) {
+    out_i[p] = -1;
+    if (out_s) out_s[p] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k for many short rows (prefill): one wave per row, four rows per block, no block
+// barriers.  Same selection as topk_radix (8 passes of 4-bit digits on lane-private LDS
+// columns, early exit), but the per-digit totals come from a 4-lane quad reduction and the
+// compaction walks the row once in index order, 64 keys per ballot, carrying the running
+// counts of selected and of equal keys (ties to the lower entry index).
+// Keys of lane l: indices j*64 + l; the first KPL strides stay in registers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_wave_sync() {
+  // all LDS operations of this wave done before the next ones are issued
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ int quad_sum(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  return x;
+}
+
+template <int KPL>
+__global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ scores,
+                                                 const int* __restrict__ q_pos0,
+                                                 const int* __restrict__ n_pool,
+                                                 int* __restrict__ topk_idx,
+                                                 float* __restrict__ topk_score, int rows, int T,
+                                                 int N_cap, int m, int k) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][16][64];
+  __shared__ __attribute__((aligned(16))) int tots[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;  // wave-uniform; the kernel has no block barrier
+  const int b = row / T, t = row % T;
+  const int V = visible_entries(q_pos0, n_pool, b, t, m, N_cap);
+  const float* s = scores + static_cast<size_t>(row) * N_cap;
+  int* out_i = topk_idx + static_cast<size_t>(row) * k;
+  float* out_s = topk_score ? topk_score + static_cast<size_t>(row) * k : nullptr;
+  const int kk = min(k, V);
+
+  if (kk == V) {
+    for (int p = lane; p < k; p += 64) {
+      out_i[p] = p < V ? p : -1;
+      if (out_s) out_s[p] = p < V ? s[p] : 0.f;
+    }
+    return;
+  }
+
+  const int n_str = (V + 63) / 64;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int i = j * 64 + lane;
+    key[j] = (j < n_str && i < V) ? score_key(s[i]) : 0u;
+  }
+  const int n_inv = KPL * 64 - min(V, KPL * 64);
+
+  uint32_t* hc = &hist[wave][0][lane];
+#pragma unroll
+  for (int d = 0; d < 16; ++d) hc[d * 64] = 0;
+  // reduction role: lane = 4*d + q sums columns 16q .. 16q+15 of digit d
+  const int rd = lane >> 2, rq = lane & 3;
+  uint4* rsum = reinterpret_cast<uint4*>(&hist[wave][rd][rq * 16]);
+
+  uint32_t prefix = 0, mask = 0;
+  int remaining = kk;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 28 - 4 * pass;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      atomicAdd(hc + ((key[j] >> shift) & 15u) * 64,
+                static_cast<uint32_t>((key[j] & mask) == prefix));
+    for (int j = KPL; j < n_str; ++j) {
+      const int i = j * 64 + lane;
+      if (i < V) {
+        const uint32_t kj = score_key(s[i]);
+        atomicAdd(hc + ((kj >> shift) & 15u) * 64, static_cast<uint32_t>((kj & mask) == prefix));
+      }
+    }
+    lds_wave_sync();
+    int c = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 h = rsum[v];
+      c += static_cast<int>(h.x + h.y + h.z + h.w);
+      rsum[v] = make_uint4(0, 0, 0, 0);
+    }
+    c = quad_sum(c);
+    if (rd == 0 && prefix == 0u) c -= n_inv;  // empty register slots (key 0)
+    if (rq == 0) tots[wave][rd] = c;
+    lds_wave_sync();
+    int tv[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int4 q4 = reinterpret_cast<const int4*>(&tots[wave][0])[v];
+      tv[4 * v] = q4.x; tv[4 * v + 1] = q4.y; tv[4 * v + 2] = q4.z; tv[4 * v + 3] = q4.w;
+    }
+    int above = 0, digit = 0, in_digit = 0;
+    bool found = false;
+#pragma unroll
+    for (int d = 15; d >= 0; --d) {
+      if (!found) {
+        if (above + tv[d] >= remaining) { digit = d; in_digit = tv[d]; found = true; }
+        else above += tv[d];
+      }
+    }
+    remaining -= above;
+    prefix |= static_cast<uint32_t>(digit) << shift;
+    mask |= 15u << shift;
+    if (in_digit == remaining) break;
+    lds_wave_sync();  // tots read before the next pass rewrites them
+  }
+
+  // one index-ordered walk over the row
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int eq_seen = 0, out_pos = 0;
+  auto emit = [&](int i, bool ok, uint32_t kj) {
+    const uint32_t km = kj & mask;
+    const bool gt = ok && km > prefix;
+    const bool eq = ok && km == prefix;
+    const unsigned long long eb = __ballot(eq);
+    const bool sel = gt || (eq && eq_seen + __popcll(eb & below) < remaining);
+    eq_seen += __popcll(eb);
+    const unsigned long long sb = __ballot(sel);
+    const int pos = out_pos + __popcll(sb & below);
+    if (sel && pos < k) {  // exactly kk keys are selected; the bound only guards the buffer
+      out_i[pos] = i;
+      if (out_s) out_s[pos] = s[i];
+    }
+    out_pos += __popcll(sb);
+  };
+#pragma unroll
+  for (int j = 0; j < KPL; ++j)
+    if (j < n_str) emit(j * 64 + lane, key[j] != 0u, key[j]);
+  for (int j = KPL; j < n_str; ++j) {
+    const int i = j * 64 + lane;
+    const bool ok = i < V;
+    emit(i, ok, ok ? score_key(s[i]) : 0u);
+  }
+  for (int p = kk + lane; p < k; p += 64) {
     out_i[p] = -1;
     if (out_s) out_s[p] = 0.f;
   }
@@ -322,12 +688,20 @@ __global__ void __launch_bounds__(NT) topk_kernel(const float* __restrict__ scor
 hipError_t launch_topk(const float* scores, const int* q_pos0, const int* n_pool, int* topk_idx,
                        float* topk_score, int B, int T, int N_cap, int m, int k, hipStream_t st) {
   if (B == 0 || T == 0) return hipSuccess;
-  if (N_cap > 8192)
-    hipLaunchKernelGGL((topk_kernel<1024>), dim3(B * T), dim3(1024), 0, st, scores, q_pos0, n_pool,
-                       topk_idx, topk_score, T, N_cap, m, k);
-  else
-    hipLaunchKernelGGL((topk_kernel<256>), dim3(B * T), dim3(256), 0, st, scores, q_pos0, n_pool,
-                       topk_idx, topk_score, T, N_cap, m, k);
+  const int rows = B * T;
+  if (N_cap > 8192 && rows < 2048) {
+    // few long rows (decode): one block of 1024 threads per row
+    hipLaunchKernelGGL((topk_radix<1024, 32>), dim3(rows), dim3(1024), 0, st, scores, q_pos0,
+                       n_pool, topk_idx, topk_score, T, N_cap, m, k);
+  } else {
+    const dim3 grid(div_up(rows, 4));
+    if (N_cap <= 2048)
+      hipLaunchKernelGGL((topk_wave<32>), grid, dim3(256), 0, st, scores, q_pos0, n_pool,
+                         topk_idx, topk_score, rows, T, N_cap, m, k);
+    else  // strides past the 64 in registers are re-read from the score row on every pass
+      hipLaunchKernelGGL((topk_wave<64>), grid, dim3(256), 0, st, scores, q_pos0, n_pool,
+                         topk_idx, topk_score, rows, T, N_cap, m, k);
+  }
   return hipGetLastError();
 }
 

@@ -105,10 +105,16 @@ def test_swa_concat_in_place_and_clipped():
 
 # ---------------------------------------------------------------------------- index + top-k
 
-def _topk_case(dt, B, T, nI, cI, N_cap, k, m, q_pos0, n_pool, seed, ties=False):
+def _topk_case(dt, B, T, nI, cI, N_cap, k, m, q_pos0, n_pool, seed, ties=False,
+               few_rows=()):
     q = normal("q_idx", (B, T, nI, cI), seed)
     w = normal("w_idx", (B, T, nI), seed).astype(np.float32)
     kp = normal("k_pool", (B, N_cap, cI), seed)
+    for b in few_rows:
+        # every key row is one of 6 distinct rows: only 6 distinct scores per query, so the
+        # k-th slot sits inside a block of thousands of exact ties (lowest indices must win)
+        pick = np.random.default_rng(seed + b).integers(0, 6, N_cap)
+        kp[b] = kp[b, :6][pick]
     if ties:
         # positive queries and weights; entries >= 10 are all -1, so their score is exactly 0:
         # the k-th slot falls inside a block of exact zero ties (lowest indices must win);
@@ -157,6 +163,18 @@ def test_index_topk_prefill_offset_batches():
 def test_index_topk_decode_split():
     # T = 1 per sequence: the split-N decode path; n_pool caps visibility
     _topk_case("bf16", 3, 1, 64, 128, 2300, 512, 4, [4000, 9000, 200], [1000, 2250, 50], 8)
+
+
+def test_index_topk_decode_long_rows():
+    # V = 40000 and 33001: more keys than the top-k kernel keeps in registers and more than
+    # one compaction segment; sequence 1 has only 6 distinct scores (exact ties everywhere)
+    _topk_case("bf16", 2, 1, 64, 128, 40000, 512, 4, [159999, 132003], [40000, 40000], 11,
+               few_rows=(1,))
+
+
+def test_index_topk_small_T_stream_path():
+    # T = 3 queries per sequence on the streaming scorer (T < 8), ragged entry counts
+    _topk_case("bf16", 2, 3, 64, 128, 3000, 300, 4, [7001, 4096], [1800, 3000], 12)
 
 
 def test_index_topk_exact_ties():
