@@ -34,12 +34,19 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 constexpr int IX_ROW = IX_CI * 2;  // bytes per indexer key row
 
-// Raw buffer descriptor over [base, base + bytes): reads past the end return zeros.
+// Raw buffer descriptor over [base, base + bytes): reads past the end return zeros.  The
+// arguments are made wave-uniform explicitly, so the descriptor lives in SGPRs (a descriptor
+// the compiler cannot prove uniform is applied lane group by lane group in a loop).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ rsrc_t make_rs(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<unsigned long long>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0),
+                                           static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           0x00020000);
 }
 
 // Sum of a value across the two 32-lane halves of the wave.
@@ -122,51 +129,94 @@ __global__ void __launch_bounds__(512, 1) index_score_mfma(
       for (int e = 0; e < 16; ++e) wv[hb][e] = wp[(e >> 2) * 8 + (e & 3)];
     }
   }
-  float* srow = scores + (static_cast<size_t>(b) * T + tq) * N_cap;
+  // Score stores go through a descriptor over this query's row: lanes with nothing to store
+  // get an offset past its end, so every sub-tile issues exactly one store instruction and
+  // the tile loop can wait for its LDS-DMA loads without waiting for the stores behind them.
+  const rsrc_t srs = make_rs(scores + (static_cast<size_t>(b) * T + min(tq, T - 1)) * N_cap,
+                             static_cast<unsigned>(N_cap) * 4u);
   const int rsw = l32 & 15;  // B-operand chunk swizzle of this lane's row
 
+  // Software pipeline over 32-entry sub-tiles: the MFMAs of sub-tile j are interleaved with
+  // the ReLU-weighted head sum of sub-tile j-1 (two accumulator sets), so the matrix core and
+  // the vector ALU work at the same time within the wave.
+  f32x16_t accA[2], accB[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accB[hb][e] = 0.f;
+  int n_pend = -1;  // entry of this lane's pending score (none yet)
+  const f32x16_t zero = {};
+
+  auto scores_of = [&](f32x16_t (&acc)[2], const unsigned char* kt, int sub) {
+    const unsigned char* brow = kt + (sub * 32 + l32) * IX_ROW;
+    bf16x8_t bk[IX_CI / 16];
+#pragma unroll
+    for (int ks = 0; ks < IX_CI / 16; ++ks)
+      bk[ks] = *reinterpret_cast<const bf16x8_t*>(brow + (((2 * ks + half) ^ rsw) << 4));
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+      acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][0], bk[0], zero, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < IX_CI / 16; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][ks], bk[ks], acc[hb], 0, 0, 0);
+  };
+  // ReLU as an integer max: non-negative floats are non-negative integers, and -0 -> +0
+  auto head_sum = [&](const f32x16_t (&acc)[2], int n) {
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      p0 += wv[0][e] * __int_as_float(max(__float_as_int(acc[0][e]), 0));
+      p1 += wv[1][e] * __int_as_float(max(__float_as_int(acc[1][e]), 0));
+      p2 += wv[0][e + 1] * __int_as_float(max(__float_as_int(acc[0][e + 1]), 0));
+      p3 += wv[1][e + 1] * __int_as_float(max(__float_as_int(acc[1][e + 1]), 0));
+    }
+    const float part = xhalf_sum((p0 + p1) + (p2 + p3));
+    const bool ok = half == 0 && n >= 0 && n < V;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srs,
+                                          ok ? static_cast<unsigned>(n) * 4u : 0xFFFFFFF0u, 0, 0);
+  };
+  auto interleave = []() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the sub-tile's 8 LDS reads first,
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                       // then 2 MFMAs : 9 VALU, 8 times
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+    }
+  };
+
+  bool stored = false;  // the previous tile issued its 4 score stores after its loads
   for (int tile = 0; tile < n_tiles; ++tile) {
-    // this wave's part of tile `tile` has landed (and its earlier score stores are done);
-    // after the barrier every part has, and every wave is past tile-1, whose slot is reused
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // This wave's part of tile `tile` has landed: vector memory operations complete in issue
+    // order, and only the previous tile's 4 score stores were issued after those loads.  After
+    // the barrier every part has, and every wave is past tile-1, whose slot is reused.
+    if (stored)
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (tile + 1 < n_tiles) issue(tile + 1, (tile + 1) & 1);
     const unsigned char* kt = ktile[tile & 1];
     const int n0 = tile * IX_TILE;
-    if (n0 >= V) continue;  // wave-uniform: this query sees none of the tile
+    stored = n0 < V;
+    if (!stored) continue;  // wave-uniform: this query sees none of the tile (only at the end)
 
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      f32x16_t acc[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[hb][e] = 0.f;
-      // all B fragments of the sub-tile first: the LDS latency overlaps the MFMAs
-      const unsigned char* brow = kt + (sub * 32 + l32) * IX_ROW;
-      bf16x8_t bk[IX_CI / 16];
-#pragma unroll
-      for (int ks = 0; ks < IX_CI / 16; ++ks)
-        bk[ks] = *reinterpret_cast<const bf16x8_t*>(brow + (((2 * ks + half) ^ rsw) << 4));
-#pragma unroll
-      for (int ks = 0; ks < IX_CI / 16; ++ks)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][ks], bk[ks], acc[hb], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 LDS reads ...
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // ... ahead of the 16 MFMAs
-      // ReLU as an integer max: non-negative floats are non-negative integers, and -0 -> +0
-      float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p0 += wv[0][e] * __int_as_float(max(__float_as_int(acc[0][e]), 0));
-        p1 += wv[1][e] * __int_as_float(max(__float_as_int(acc[1][e]), 0));
-      }
-      const float part = xhalf_sum(p0 + p1);
-      const int n = n0 + sub * 32 + l32;
-      if (half == 0 && n < V) srow[n] = part;
-    }
+    scores_of(accA, kt, 0);
+    head_sum(accB, n_pend);
+    interleave();
+    scores_of(accB, kt, 1);
+    head_sum(accA, n0 + l32);
+    interleave();
+    scores_of(accA, kt, 2);
+    head_sum(accB, n0 + 32 + l32);
+    interleave();
+    scores_of(accB, kt, 3);
+    head_sum(accA, n0 + 64 + l32);
+    interleave();
+    n_pend = n0 + 96 + l32;
   }
+  head_sum(accB, n_pend);
 }
 
 // ---------------------------------------------------------------------------
