@@ -122,6 +122,7 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_pool, co
  *
  *   kv_raw : [B, S_new, D] dtype.  kv_win : [B, S_cap, D] dtype.
  *   kv_pos0, new_pos0 : [B] int32 device arrays.  D even, rope_dim even and <= D.
+ *   B * S_new * D below 2^32 (DSV4_ERR_UNSUPPORTED otherwise).
  */
 int swa_concat(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0, int B,
                int S_new, int S_cap, int D, int rope_dim, double rope_theta,

@@ -134,6 +134,9 @@ int swa_concat(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* 
   REQUIRE(D >= 2 && D % 2 == 0, "D must be even and >= 2");
   if (int rc = check_rope(rope_dim, D, rope_theta)) return rc;
   if (B == 0 || S_new == 0 || S_cap == 0) return ok();
+  if (static_cast<long long>(B) * S_new * D >= (1LL << 32))
+    return fail(DSV4_ERR_UNSUPPORTED, "B*S_new*D = %lld elements, at most 2^32 - 1",
+                static_cast<long long>(B) * S_new * D);
   REQUIRE(kv_raw && kv_win && kv_pos0 && new_pos0, "null required pointer");
   REQUIRE(aligned16(kv_raw) && aligned16(kv_win), "pointers must be 16-byte aligned");
   return launched(dsv4::launch_swa(kv_raw, kv_win, kv_pos0, new_pos0, B, S_new, S_cap, D, rope_dim,

@@ -113,10 +113,23 @@ __device__ __forceinline__ float load1<bf16_t>(const bf16_t* p) { return bf16_to
 // ---------------------------------------------------------------------------
 // RoPE on interleaved pairs of the trailing r channels (pair i = channels C-r+2i, C-r+2i+1,
 // frequency theta^(-2i/r)).  Frequencies and angles are formed in double precision and the
-// angle is reduced modulo 2*pi in double; sin/cos of the reduced angle and the rotation
-// itself are evaluated in fp32 (error ~1e-7 for any position below 2^31).
+// angle is reduced modulo one turn in double; the rotation is evaluated in fp32.  sin/cos of
+// the reduced angle: the fp32 library functions (error ~1e-7) on the fp32 path, the hardware
+// sine / cosine of the reduced turn on the bf16 path (its error is far below bf16 rounding).
 // ---------------------------------------------------------------------------
 constexpr int kMaxRope = 256;
+
+// theta^(-2i/r) for i < r/2, formed on the host in double precision; kernels take it by value.
+struct RopeFreq {
+  double inv[kMaxRope / 2];
+};
+
+inline RopeFreq make_rope_freq(int r, double theta) {
+  RopeFreq f{};
+  for (int i = 0; i < r / 2 && i < kMaxRope / 2; ++i)
+    f.inv[i] = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(r));
+  return f;
+}
 
 // Fill inv_freq[0 .. r/2) (one block-wide table); the caller synchronises before use.
 __device__ __forceinline__ void rope_table(double* inv_freq, int r, double theta) {
@@ -124,15 +137,20 @@ __device__ __forceinline__ void rope_table(double* inv_freq, int r, double theta
     inv_freq[i] = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(r));
 }
 
+template <bool FAST = false>
 __device__ __forceinline__ void rope_cs(double ang, float& c, float& s) {
-  const double two_pi = 6.283185307179586476925286766559;
-  const double k = rint(ang * (1.0 / two_pi));
-  const float red = static_cast<float>(fma(-k, two_pi, ang));
-  sincosf(red, &s, &c);
+  const double turns = ang * 0.15915494309189533576888376337251;  // ang / (2 pi)
+  const float frac = static_cast<float>(turns - rint(turns));    // [-1/2, 1/2] turn
+  if constexpr (FAST) {
+    c = __builtin_amdgcn_cosf(frac);  // hardware cos / sin take turns
+    s = __builtin_amdgcn_sinf(frac);
+  } else {
+    sincosf(frac * 6.283185307179586f, &s, &c);
+  }
 }
 
 // Rotate the pairs of an N-channel chunk that starts at channel c0 (c0 even) at position pos.
-template <int N>
+template <int N, bool FAST = false>
 __device__ __forceinline__ void rope_chunk(float (&v)[N], int c0, int C, int r, double pos,
                                            const double* inv_freq) {
   if (r == 0 || c0 + N <= C - r) return;
@@ -141,7 +159,7 @@ __device__ __forceinline__ void rope_chunk(float (&v)[N], int c0, int C, int r, 
     const int ch = c0 + i;
     if (ch >= C - r) {
       float c, s;
-      rope_cs(pos * inv_freq[(ch - (C - r)) >> 1], c, s);
+      rope_cs<FAST>(pos * inv_freq[(ch - (C - r)) >> 1], c, s);
       const float a = v[i], b = v[i + 1];
       v[i] = a * c - b * s;
       v[i + 1] = a * s + b * c;

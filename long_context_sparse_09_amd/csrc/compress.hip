@@ -25,10 +25,10 @@ template <typename T, int VEC>
 __global__ void __launch_bounds__(256) compress_kernel(
     const T* __restrict__ x, const T* __restrict__ gate, const float* __restrict__ bias,
     T* __restrict__ pool, int S, int C, int m, int overlap, int e0, int e1, int N_cap, int r,
-    double theta, long long pos_off, int G, int P, int E) {
+    const RopeFreq rf, long long pos_off, int G, int P, int E) {
   extern __shared__ float red[];  // [E*P*G][3*VEC] partial states when P > 1
   __shared__ double inv_freq[kMaxRope / 2];
-  rope_table(inv_freq, r, theta);
+  for (int i = threadIdx.x; i < r / 2; i += blockDim.x) inv_freq[i] = rf.inv[i];
   const int tid = threadIdx.x;
   const int g = tid % G;
   const int p = (tid / G) % P;
@@ -49,35 +49,48 @@ __global__ void __launch_bounds__(256) compress_kernel(
 
   if (active) {
     const size_t row0 = static_cast<size_t>(b) * S;
-    for (int s = s0; s < s1; ++s) {
-      const int j = lo + s;
-      if (j < 0 || j >= S) continue;
-      float xv[VEC], gv[VEC];
-      Chunk<T>::template load<VEC>(x + (row0 + j) * C + c0, xv);
-      Chunk<T>::template load<VEC>(gate + (row0 + j) * C + c0, gv);
-      if (bias != nullptr) {
-        float bv[VEC];
-        Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s) * C + c0, bv);
+    // Slots in groups of U: the 2U row loads of a group are all issued before any is used,
+    // so a thread keeps 2U independent loads in flight instead of one slot's latency at a time.
+    constexpr int U = 8;
+    for (int sg = s0; sg < s1; sg += U) {
+      float xv[U][VEC], gv[U][VEC];
+      bool ok[U];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) gv[i] += bv[i];
+      for (int u = 0; u < U; ++u) {
+        const int s = sg + u;
+        const int j = lo + s;
+        ok[u] = s < s1 && j >= 0 && j < S;
+        const size_t jr = row0 + (ok[u] ? j : 0);  // a valid row; unused when !ok
+        Chunk<T>::template load<VEC>(x + jr * C + c0, xv[u]);
+        Chunk<T>::template load<VEC>(gate + jr * C + c0, gv[u]);
       }
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const float a = gv[i] * kLog2e;
-        const float d = exp2f(-fabsf(a - mx[i]));  // 0 on the first slot (mx = -inf)
-        if (a > mx[i]) {
-          sm[i] = sm[i] * d + 1.f;
-          acc[i] = acc[i] * d + xv[i];
-          mx[i] = a;
-        } else {
-          sm[i] += d;
-          acc[i] += d * xv[i];
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        if (bias != nullptr) {
+          float bv[VEC];
+          Chunk<float>::template load<VEC>(bias + static_cast<size_t>(sg + u) * C + c0, bv);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) gv[u][i] += bv[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float a = gv[u][i] * kLog2e;
+          const float d = exp2f(-fabsf(a - mx[i]));  // 0 on the first slot (mx = -inf)
+          if (a > mx[i]) {
+            sm[i] = sm[i] * d + 1.f;
+            acc[i] = acc[i] * d + xv[u][i];
+            mx[i] = a;
+          } else {
+            sm[i] += d;
+            acc[i] += d * xv[u][i];
+          }
         }
       }
     }
   }
 
-  __syncthreads();  // inv_freq ready
+  __syncthreads();  // inv_freq staged
   if (P > 1) {
     float* mine = red + static_cast<size_t>(tid) * 3 * VEC;
 #pragma unroll
@@ -105,7 +118,7 @@ __global__ void __launch_bounds__(256) compress_kernel(
 #pragma unroll
   for (int i = 0; i < VEC; ++i) out[i] = acc[i] / sm[i];
   const double pos = static_cast<double>((static_cast<long long>(w) + 1) * m - 1 + pos_off);
-  rope_chunk<VEC>(out, c0, C, r, pos, inv_freq);
+  rope_chunk<VEC, sizeof(T) == 2>(out, c0, C, r, pos, inv_freq);
   Chunk<T>::template store<VEC>(pool + (static_cast<size_t>(b) * N_cap + w) * C + c0, out);
 }
 
@@ -115,9 +128,10 @@ static hipError_t compress_t(const void* x, const void* gate, const float* bias,
                              double theta, long long off, hipStream_t st) {
   const int G = C / VEC;
   const int span = overlap ? 2 * m : m;
+  // long windows: split the slots over P thread groups (16+ slots each)
   int P = 1;
   if (span >= 32) P = max(1, min(256 / G, span / 16));
-  int E = max(1, 256 / (G * P));
+  const int E = max(1, 256 / (G * P));
   const int threads = G * P * E;
   const int n = e1 - e0;
   if (n <= 0) return hipSuccess;
@@ -125,7 +139,8 @@ static hipError_t compress_t(const void* x, const void* gate, const float* bias,
   size_t shmem = P > 1 ? static_cast<size_t>(threads) * 3 * VEC * sizeof(float) : 0;
   hipLaunchKernelGGL((compress_kernel<T, VEC>), grid, dim3(threads), shmem, st,
                      static_cast<const T*>(x), static_cast<const T*>(gate), bias,
-                     static_cast<T*>(pool), S, C, m, overlap, e0, e1, N_cap, r, theta, off, G, P, E);
+                     static_cast<T*>(pool), S, C, m, overlap, e0, e1, N_cap, r,
+                     make_rope_freq(r, theta), off, G, P, E);
   return hipGetLastError();
 }
 
@@ -143,43 +158,81 @@ hipError_t launch_compress(const void* x, const void* gate, const float* bias, v
 
 // ---------------------------------------------------------------------------
 // swa_concat: rotate raw K=V rows at their positions into the window buffer.
-// One thread per VEC-channel chunk of one row.
+//
+// The chunks of a row that hold no rotary channel (the first Gn of its G VEC-channel chunks)
+// are a plain copy; the Gr = G - Gn trailing ones are rotated.  The grid is split in two
+// regions so that no wavefront mixes the two kinds: blocks below nb_copy copy, the rest
+// rotate (inv_freq staged in LDS).  Each thread handles SWA_U chunks a block-stride apart and
+// issues all their loads before any store.  Index arithmetic is 32-bit (the host checks the
+// chunk counts): 64-bit division is a long software sequence on this target.
 // ---------------------------------------------------------------------------
+constexpr int SWA_U = 4;
+
 template <typename T, int VEC>
 __global__ void __launch_bounds__(256) swa_kernel(const T* __restrict__ kv_raw, T* kv_win,
                                                   const int* __restrict__ kv_pos0,
                                                   const int* __restrict__ new_pos0, int S_new,
-                                                  int S_cap, int D, int r, double theta,
-                                                  long long pos_off, long long total) {
+                                                  int S_cap, int D, int r, const RopeFreq rf,
+                                                  long long pos_off, int Gn, unsigned n_copy,
+                                                  unsigned n_rot, unsigned nb_copy) {
   __shared__ double inv_freq[kMaxRope / 2];
-  rope_table(inv_freq, r, theta);
-  __syncthreads();
-  const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= total) return;
-  const int G = D / VEC;
-  const int g = static_cast<int>(gid % G);
-  const long long row = gid / G;  // b * S_new + i
-  const int i = static_cast<int>(row % S_new);
-  const int b = static_cast<int>(row / S_new);
-  const long long seq = static_cast<long long>(new_pos0[b]) + i;
-  const long long dst = seq - kv_pos0[b];
-  if (dst < 0 || dst >= S_cap) return;
-  float v[VEC];
-  Chunk<T>::template load<VEC>(kv_raw + row * D + g * VEC, v);
-  rope_chunk<VEC>(v, g * VEC, D, r, static_cast<double>(seq + pos_off), inv_freq);
-  Chunk<T>::template store<VEC>(kv_win + (static_cast<long long>(b) * S_cap + dst) * D + g * VEC, v);
+  const unsigned G = static_cast<unsigned>(D / VEC);
+  const bool rot = blockIdx.x >= nb_copy;  // block-uniform
+  const unsigned Gk = rot ? G - Gn : Gn;   // chunks of this kind per row
+  const unsigned total = rot ? n_rot : n_copy;
+  const unsigned blk = rot ? blockIdx.x - nb_copy : blockIdx.x;
+  if (rot) {
+    for (int i = threadIdx.x; i < r / 2; i += blockDim.x) inv_freq[i] = rf.inv[i];
+    __syncthreads();
+  }
+  const unsigned base = blk * blockDim.x * SWA_U + threadIdx.x;
+  float v[SWA_U][VEC];
+#pragma unroll
+  for (int u = 0; u < SWA_U; ++u) {
+    const unsigned gid = base + u * blockDim.x;
+    const unsigned ld = gid < total ? gid : total - 1;  // a valid chunk; unused past the end
+    const unsigned row = ld / Gk;
+    const unsigned g = (rot ? Gn : 0) + (ld - row * Gk);
+    Chunk<T>::template load<VEC>(kv_raw + (static_cast<size_t>(row) * G + g) * VEC, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < SWA_U; ++u) {
+    const unsigned gid = base + u * blockDim.x;
+    if (gid >= total) break;
+    const unsigned row = gid / Gk;  // b * S_new + i
+    const int g = static_cast<int>((rot ? Gn : 0) + (gid - row * Gk));
+    const int b = static_cast<int>(row / static_cast<unsigned>(S_new));
+    const int i = static_cast<int>(row - static_cast<unsigned>(b) * S_new);
+    const long long seq = static_cast<long long>(new_pos0[b]) + i;
+    const long long dst = seq - kv_pos0[b];
+    if (dst < 0 || dst >= S_cap) continue;
+    if (rot)
+      rope_chunk<VEC, sizeof(T) == 2>(v[u], g * VEC, D, r, static_cast<double>(seq + pos_off),
+                                      inv_freq);
+    Chunk<T>::template store<VEC>(kv_win + (static_cast<long long>(b) * S_cap + dst) * D + g * VEC,
+                                  v[u]);
+  }
 }
 
 template <typename T, int VEC>
 static hipError_t swa_t(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0,
                         int B, int S_new, int S_cap, int D, int r, double theta, long long off,
                         hipStream_t st) {
-  const long long total = static_cast<long long>(B) * S_new * (D / VEC);
-  if (total == 0) return hipSuccess;
+  const long long rows = static_cast<long long>(B) * S_new;
+  const int G = D / VEC;
+  const int Gn = (D - r) / VEC;  // chunks with no rotary channel
+  const long long n_copy = rows * Gn, n_rot = rows * (G - Gn);
+  if (rows == 0) return hipSuccess;
+  if (rows * G >= (1LL << 31)) return hipErrorInvalidValue;  // 32-bit chunk indices
   const int threads = 256;
-  hipLaunchKernelGGL((swa_kernel<T, VEC>), dim3(static_cast<unsigned>((total + threads - 1) / threads)),
+  const long long per_block = static_cast<long long>(threads) * SWA_U;
+  const long long nb_copy = (n_copy + per_block - 1) / per_block;
+  const long long nb_rot = (n_rot + per_block - 1) / per_block;
+  hipLaunchKernelGGL((swa_kernel<T, VEC>), dim3(static_cast<unsigned>(nb_copy + nb_rot)),
                      dim3(threads), 0, st, static_cast<const T*>(kv_raw), static_cast<T*>(kv_win),
-                     kv_pos0, new_pos0, S_new, S_cap, D, r, theta, off, total);
+                     kv_pos0, new_pos0, S_new, S_cap, D, r, make_rope_freq(r, theta), off, Gn,
+                     static_cast<unsigned>(n_copy), static_cast<unsigned>(n_rot),
+                     static_cast<unsigned>(nb_copy));
   return hipGetLastError();
 }
 
