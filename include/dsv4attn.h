@@ -129,6 +129,13 @@ int swa_concat(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* 
                long long rope_pos_offset, int dtype, void* stream);
 
 /*
+ * attend_workspace_size - bytes of the optional workspace of csa_attend / hca_attend for B*T
+ * queries of H heads x D channels on the current device; 0 when the split path does not
+ * apply (many queries, or a shape outside the bf16 64 x 512 path), in which case NULL is fine.
+ */
+size_t attend_workspace_size(int B, int T, int H, int D);
+
+/*
  * csa_attend - CSA core attention over [window || selected entries] ("Hybrid attention
  * (§2.3)", shared skeleton; "Attention mask layout", CSA paragraph).
  *
@@ -144,12 +151,17 @@ int swa_concat(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* 
  *   pool: [B, N_cap, D] dtype, rotated.  topk_idx : [B, T, k] int32.  sink : [H] float32.
  *   kv_pos0, q_pos0 : [B] int32 device arrays.  out : [B, T, H, D] dtype.
  *   scale <= 0 selects 1/sqrt(D).  Requires window >= 1, D even, rope_dim even <= D.
+ *   workspace : NULL, or caller-owned device scratch of at least
+ *     attend_workspace_size(B, T, H, D) bytes (16-byte aligned; DSV4_ERR_WORKSPACE when
+ *     smaller).  With it, batches of few queries (decode) cut each query's keys into
+ *     ranges attended by separate workgroups and merged afterwards; the result is the same
+ *     up to fp32 rounding order.  Its contents are scratch between calls.
  */
 int csa_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
                int N_cap, const int* topk_idx, int k, const float* sink, const int* q_pos0,
                void* out, int B, int T, int H, int D, int window, int rope_dim,
-               double rope_theta, long long rope_pos_offset, float scale, int dtype,
-               void* stream);
+               double rope_theta, long long rope_pos_offset, float scale, void* workspace,
+               size_t workspace_bytes, int dtype, void* stream);
 
 /*
  * hca_attend - HCA core attention over [window || every visible entry] ("Hybrid attention
@@ -164,8 +176,8 @@ int csa_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
 int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
                int N_cap, const int* n_pool, int m_hca, const float* sink, const int* q_pos0,
                void* out, int B, int T, int H, int D, int window, int rope_dim,
-               double rope_theta, long long rope_pos_offset, float scale, int dtype,
-               void* stream);
+               double rope_theta, long long rope_pos_offset, float scale, void* workspace,
+               size_t workspace_bytes, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -110,26 +110,40 @@ def swa_concat(kv_raw, kv_win, kv_pos0, new_pos0, rope_dim: int, rope_theta: flo
         float(rope_theta), int(rope_pos_offset), _dtype(kv_raw), _stream(stream)))
 
 
+def attend_workspace_size(B: int, T: int, H: int, D: int) -> int:
+    return int(lib().attend_workspace_size(B, T, H, D))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
 def csa_attend(q, kv_win, kv_pos0, pool, topk_idx, sink, q_pos0, out, window: int,
                rope_dim: int, rope_theta: float, rope_pos_offset: int = 0, scale: float = 0.0,
-               stream=None) -> None:
+               workspace=None, stream=None) -> None:
     """q [B,T,H,D]; kv_win [B,S_kv,D]; pool [B,N_cap,D]; topk_idx [B,T,k]; sink [H] fp32;
-    kv_pos0/q_pos0 [B] int32; out [B,T,H,D]."""
+    kv_pos0/q_pos0 [B] int32; out [B,T,H,D]; workspace: None or a uint8 device tensor of
+    attend_workspace_size bytes."""
     B, T, H, D = q.shape
+    wp, wb = _ws(workspace)
     _check("csa_attend", lib().csa_attend(
         _ptr(q), _ptr(kv_win), _ptr(kv_pos0), kv_win.shape[1], _ptr(pool), pool.shape[1],
         _ptr(topk_idx), topk_idx.shape[2], _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D,
-        window, rope_dim, float(rope_theta), int(rope_pos_offset), float(scale), _dtype(q),
-        _stream(stream)))
+        window, rope_dim, float(rope_theta), int(rope_pos_offset), float(scale), wp, wb,
+        _dtype(q), _stream(stream)))
 
 
 def hca_attend(q, kv_win, kv_pos0, pool, n_pool, m_hca: int, sink, q_pos0, out, window: int,
                rope_dim: int, rope_theta: float, rope_pos_offset: int = 0, scale: float = 0.0,
-               stream=None) -> None:
+               workspace=None, stream=None) -> None:
     """As csa_attend, over every visible pool entry; pool None (and N_cap 0) = sliding only."""
     B, T, H, D = q.shape
     N_cap = 0 if pool is None else pool.shape[1]
+    wp, wb = _ws(workspace)
     _check("hca_attend", lib().hca_attend(
         _ptr(q), _ptr(kv_win), _ptr(kv_pos0), kv_win.shape[1], _ptr(pool), N_cap, _ptr(n_pool),
         m_hca, _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D, window, rope_dim,
-        float(rope_theta), int(rope_pos_offset), float(scale), _dtype(q), _stream(stream)))
+        float(rope_theta), int(rope_pos_offset), float(scale), wp, wb, _dtype(q),
+        _stream(stream)))

@@ -26,12 +26,13 @@ SIGNATURES = {
                         c_int, c_void_p], c_int),
     "swa_concat": ([c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                     c_double, c_ll, c_int, c_void_p], c_int),
+    "attend_workspace_size": ([c_int, c_int, c_int, c_int], c_size_t),
     "csa_attend": ([c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_int,
                     c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
-                    c_double, c_ll, c_float, c_int, c_void_p], c_int),
+                    c_double, c_ll, c_float, c_void_p, c_size_t, c_int, c_void_p], c_int),
     "hca_attend": ([c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_int,
                     c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
-                    c_double, c_ll, c_float, c_int, c_void_p], c_int),
+                    c_double, c_ll, c_float, c_void_p, c_size_t, c_int, c_void_p], c_int),
 }
 
 _lib = None

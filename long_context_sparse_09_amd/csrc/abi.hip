@@ -145,7 +145,8 @@ int swa_concat(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* 
                   "swa_concat");
 }
 
-static int attend_common(dsv4::AttendArgs& a, void* stream, const char* name) {
+static int attend_common(dsv4::AttendArgs& a, void* workspace, size_t workspace_bytes,
+                         void* stream, const char* name) {
   REQUIRE(dtype_ok(a.dtype), "dtype %d", a.dtype);
   REQUIRE(a.B >= 0 && a.T >= 0 && a.S_kv >= 0 && a.N_cap >= 0, "negative size");
   REQUIRE(a.H >= 1 && a.D >= 2 && a.D % 2 == 0, "H >= 1 and even D >= 2 required");
@@ -158,6 +159,18 @@ static int attend_common(dsv4::AttendArgs& a, void* stream, const char* name) {
   REQUIRE(a.N_cap == 0 || a.pool, "pool required when N_cap > 0");
   REQUIRE(aligned16(a.q) && aligned16(a.kv_win) && aligned16(a.out) && (!a.pool || aligned16(a.pool)),
           "pointers must be 16-byte aligned");
+  a.n_split = 1;
+  a.part = nullptr;
+  if (workspace != nullptr) {
+    REQUIRE(aligned16(workspace), "workspace must be 16-byte aligned");
+    const size_t need = dsv4::attend_split_bytes(a.B * a.T);
+    if (workspace_bytes < need)
+      return fail(DSV4_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    if (need > 0 && dsv4::attend_uses_fast(a)) {
+      a.n_split = dsv4::attend_split_count(a.B * a.T);
+      a.part = static_cast<float*>(workspace);
+    }
+  }
   if (!dsv4::attend_uses_fast(a)) {
     if (a.D > 4096) return fail(DSV4_ERR_UNSUPPORTED, "D=%d above 4096 for the generic kernel", a.D);
     const long long max_keys = static_cast<long long>(a.window) + (a.csa ? a.k : a.N_cap);
@@ -168,30 +181,35 @@ static int attend_common(dsv4::AttendArgs& a, void* stream, const char* name) {
   return launched(dsv4::launch_attend(a, static_cast<hipStream_t>(stream)), name);
 }
 
+size_t attend_workspace_size(int B, int T, int H, int D) {
+  if (B <= 0 || T <= 0 || !dsv4::attend_fast(H, D, 0, 1)) return 0;
+  return dsv4::attend_split_bytes(B * T);
+}
+
 int csa_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
                int N_cap, const int* topk_idx, int k, const float* sink, const int* q_pos0,
                void* out, int B, int T, int H, int D, int window, int rope_dim,
-               double rope_theta, long long rope_pos_offset, float scale, int dtype,
-               void* stream) {
+               double rope_theta, long long rope_pos_offset, float scale, void* workspace,
+               size_t workspace_bytes, int dtype, void* stream) {
   REQUIRE(k >= 1, "k must be >= 1");
   if (k > 4096) return fail(DSV4_ERR_UNSUPPORTED, "k %d above 4096", k);
   REQUIRE(B == 0 || T == 0 || topk_idx, "null topk_idx");
   dsv4::AttendArgs a{q, kv_win, kv_pos0, S_kv, pool, N_cap, topk_idx, k, nullptr, 1, sink, q_pos0,
                      out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, true,
                      {}};
-  return attend_common(a, stream, "csa_attend");
+  return attend_common(a, workspace, workspace_bytes, stream, "csa_attend");
 }
 
 int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
                int N_cap, const int* n_pool, int m_hca, const float* sink, const int* q_pos0,
                void* out, int B, int T, int H, int D, int window, int rope_dim,
-               double rope_theta, long long rope_pos_offset, float scale, int dtype,
-               void* stream) {
+               double rope_theta, long long rope_pos_offset, float scale, void* workspace,
+               size_t workspace_bytes, int dtype, void* stream) {
   REQUIRE(m_hca >= 1, "m_hca must be >= 1");
   dsv4::AttendArgs a{q, kv_win, kv_pos0, S_kv, pool, N_cap, nullptr, 0, n_pool, m_hca, sink, q_pos0,
                      out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, false,
                      {}};
-  return attend_common(a, stream, "hca_attend");
+  return attend_common(a, workspace, workspace_bytes, stream, "hca_attend");
 }
 
 }  // extern "C"

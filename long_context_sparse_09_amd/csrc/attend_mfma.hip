@@ -127,8 +127,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Per-query description, computed identically by every wave that needs it.
+// A work item is one query, or one of n_split key ranges of a query (split mode): tiles
+// tb .. tb + n_tiles - 1 of the query's keys.
 struct QInfo {
-  int b, t, r0, n_win, n_keys, n_tiles;
+  int b, t, r0, n_win, n_keys, n_tiles, tb, sp;
   long long p;
 };
 
@@ -149,17 +151,32 @@ __device__ __forceinline__ QInfo uniform(const QInfo& d) {
   u.n_win = __builtin_amdgcn_readfirstlane(d.n_win);
   u.n_keys = __builtin_amdgcn_readfirstlane(d.n_keys);
   u.n_tiles = __builtin_amdgcn_readfirstlane(d.n_tiles);
+  u.tb = __builtin_amdgcn_readfirstlane(d.tb);
+  u.sp = __builtin_amdgcn_readfirstlane(d.sp);
   const unsigned long long pu = static_cast<unsigned long long>(d.p);
   u.p = static_cast<long long>((static_cast<unsigned long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(pu >> 32))) << 32) |
                                __builtin_amdgcn_readfirstlane(static_cast<unsigned>(pu)));
   return u;
 }
 
-// Position, window rows and (HCA) visible pool entries of query qid; n_keys / n_tiles are
-// completed by set_keys() once the compressed-key count is known.
+// Tile range of a work item.  The query's keys fill nq = max(1, ceil(n_keys / 32)) tiles (an
+// empty query still runs one masked tile); split sp of n takes tiles [nq sp / n, nq (sp+1) / n),
+// or, when that is empty, one fully masked tile (index nq) so that every item runs a step.
+__device__ __forceinline__ void set_range(QInfo& d, int n_split) {
+  const int nq = max(1, (d.n_keys + ANK - 1) / ANK);
+  const int t0 = nq * d.sp / n_split, t1 = nq * (d.sp + 1) / n_split;
+  d.tb = t1 > t0 ? t0 : nq;
+  d.n_tiles = t1 > t0 ? t1 - t0 : 1;
+}
+
+// Position, window rows and (HCA) visible pool entries of the query of work item `item`;
+// for CSA, n_keys and the tile range are completed by set_keys() once the compressed-key
+// count is known.
 template <bool CSA>
-__device__ __forceinline__ QInfo query_geom(const AttendArgs& a, int qid) {
+__device__ __forceinline__ QInfo query_geom(const AttendArgs& a, int item) {
   QInfo d;
+  const int qid = item / a.n_split;
+  d.sp = item - qid * a.n_split;
   d.b = qid / a.T;
   d.t = qid % a.T;
   d.p = static_cast<long long>(load_uniform(a.q_pos0 + d.b)) + d.t;
@@ -175,13 +192,13 @@ __device__ __forceinline__ QInfo query_geom(const AttendArgs& a, int qid) {
     v = min(v, static_cast<long long>(a.N_cap));
     d.n_keys += static_cast<int>(max(v, 0LL));
   }
-  d.n_tiles = max(1, (d.n_keys + ANK - 1) / ANK);  // an empty query still runs one masked tile
+  set_range(d, a.n_split);
   return uniform(d);
 }
 
-__device__ __forceinline__ void set_keys(QInfo& d, int n_cmp) {
+__device__ __forceinline__ void set_keys(QInfo& d, int n_cmp, int n_split) {
   d.n_keys = d.n_win + n_cmp;
-  d.n_tiles = max(1, (d.n_keys + ANK - 1) / ANK);
+  set_range(d, n_split);
 }
 
 template <bool CSA, int R>  // R = rotary channels, 0 or 64 (compile-time: only those chunks move)
@@ -193,7 +210,7 @@ attend_mfma_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: roles are per wave
-  const int n_q = a.B * a.T;
+  const int n_q = a.B * a.T * a.n_split;  // work items
   const int G = gridDim.x;
   const bf16_t* qbase = static_cast<const bf16_t*>(a.q);
   int* nk = reinterpret_cast<int*>(lds + NK_OFF);  // compressed-key counts of queries [j % 8]
@@ -225,11 +242,20 @@ attend_mfma_kernel(AttendArgs a) {
       if constexpr (CSA) {  // compact the valid entries, in order
         const rsrc_t idx_rs = make_rs(a.topk_idx + (static_cast<size_t>(qi.b) * a.T + qi.t) * a.k,
                                       static_cast<unsigned>(a.k) * 4u);
+        // every load of the list first (one memory latency), then the ballot compaction
+        constexpr int NC = kMaxTopk / 64;
+        int ld[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          ld[c] = c * 64 < a.k ? static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(
+                                     idx_rs, static_cast<unsigned>(c * 64 + lane) * 4u, 0, 0))
+                               : -1;
         int base = 0;
-        for (int c0 = 0; c0 < a.k; c0 += 64) {
-          const int i = c0 + lane;
-          const int ld = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(idx_rs, static_cast<unsigned>(i) * 4u, 0, 0));
-          const int e = i < a.k ? ld : -1;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if (c * 64 >= a.k) break;  // uniform
+          const int i = c * 64 + lane;
+          const int e = i < a.k ? ld[c] : -1;
           const bool v = e >= 0 && e < a.N_cap;
           const unsigned long long m = __ballot(v);
           const int pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
@@ -237,13 +263,13 @@ attend_mfma_kernel(AttendArgs a) {
           if (v) kl[pos] = e;
           base += __popcll(m);
         }
-        set_keys(qi, base);
+        set_keys(qi, base, a.n_split);
       }
       if (lane == 0) nk[j & 7] = qi.n_keys - qi.n_win;  // compressed keys of query j
     };
     unsigned rlo = 0, rhi = 0;
-    auto tile_addr = [&]() {  // lane l < 32: address of key it*32 + l of query iq
-      const int x = it * ANK + (lane & 31);
+    auto tile_addr = [&]() {  // lane l < 32: address of key (tb + it)*32 + l of item iq
+      const int x = (qi.tb + it) * ANK + (lane & 31);
       const bf16_t* row;
       if (x < qi.n_keys) {
         if (x < qi.n_win) {
@@ -383,7 +409,7 @@ attend_mfma_kernel(AttendArgs a) {
       bool last = false;
       if (has) {
         if (first) {
-          if constexpr (CSA) set_keys(cq, __builtin_amdgcn_readfirstlane(nk[jq & 7]));
+          if constexpr (CSA) set_keys(cq, __builtin_amdgcn_readfirstlane(nk[jq & 7]), a.n_split);
           rotate_q(cq);
           m_run = sink2;
           l_run = 1.f;
@@ -421,9 +447,9 @@ attend_mfma_kernel(AttendArgs a) {
           for (int i = 0; i < 4; ++i) sacc[4 * q4 + i] += pv4[q4][i];
       }
       // online softmax over the tile's 32 keys (lane: head l32, keys (e/4)*8 + half*4 + e%4)
-      const int kbase = tq * ANK + half * 4;
+      const int kbase = (cq.tb + tq) * ANK + half * 4;
       float tmax = -INFINITY;
-      if (tq * ANK + ANK > cq.n_keys) {
+      if ((cq.tb + tq) * ANK + ANK > cq.n_keys) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kbase + (e >> 2) * 8 + (e & 3);
@@ -456,6 +482,12 @@ attend_mfma_kernel(AttendArgs a) {
       if (half == 0) {
         if (kh == 0) alph[par * 64 + head] = alpha;
         else if (last) lsum[par * 64 + head] = l_run;
+      }
+      if (a.n_split > 1 && last && half == 0 && kh == 1) {
+        // split mode: this key range's running max and sum (log2 domain, sink included)
+        float* ml = a.part + static_cast<size_t>(n_q) * AH * AD + (static_cast<size_t>(qid_of(jq)) * AH + head) * 2;
+        ml[0] = m_run;
+        ml[1] = l_run;
       }
       if (last) {
         tq = 0;
@@ -560,13 +592,43 @@ attend_mfma_kernel(AttendArgs a) {
     }
   };
 
+  // split mode: the unnormalised output of this key range, counter-rotated (the rotation is
+  // linear, so it commutes with the merge), as fp32 rows of the workspace
+  auto finish_part = [&](const QInfo& d, int item) {
+    float* po = a.part + (static_cast<size_t>(item) * AH + head) * AD + kh * (AD / 2) + half * 4;
+    const double pos = -static_cast<double>(d.p + a.pos_off);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = o[dt][gq * 4 + jj];
+        const int cl0 = dt * 32 + gq * 8;
+        if (R > 0 && kh == 1 && cl0 >= AD / 2 - R) {
+          const int pr0 = (cl0 - (AD / 2 - R)) >> 1;
+#pragma unroll
+          for (int i2 = 0; i2 < 4; i2 += 2) {
+            const double f0 = invf[pr0 + i2 / 2], f1 = invf[pr0 + 2 + i2 / 2];
+            float c, sn;
+            rope_pair(pos, half ? f1 : f0, c, sn);
+            const float xv = v[i2], yv = v[i2 + 1];
+            v[i2] = xv * c - yv * sn;
+            v[i2 + 1] = xv * sn + yv * c;
+          }
+        }
+        *reinterpret_cast<f32x4_t*>(po + cl0) = f32x4_t{v[0], v[1], v[2], v[3]};
+      }
+    }
+  };
+
   for (int s = -1;; ++s) {
     lds_barrier();  // X(s): P(s) and the rescale factor are published
     const bool has = s >= 0 && jp < n_mine;  // this step accumulates tile s
     const unsigned char* tb = lds + ((s + NSLOT) % NSLOT) * ATILE;
     if (has) {
       if (tp == 0) {
-        if constexpr (CSA) set_keys(cp, __builtin_amdgcn_readfirstlane(nk[jp & 7]));
+        if constexpr (CSA) set_keys(cp, __builtin_amdgcn_readfirstlane(nk[jp & 7]), a.n_split);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -591,7 +653,10 @@ attend_mfma_kernel(AttendArgs a) {
     if (!has) break;
     pv_steps(tb, NDT);
     if (tp + 1 == cp.n_tiles) {
-      finish(cp, 1.f / lsum[(s & 1) * 64 + head]);
+      if (a.n_split > 1)
+        finish_part(cp, qid_of(jp));
+      else
+        finish(cp, 1.f / lsum[(s & 1) * 64 + head]);
       tp = 0;
       if (++jp < n_mine) cp = query_geom<CSA>(a, qid_of(jp));
       else break;  // that was the last tile: step n_tiles - 1 is done
@@ -599,6 +664,65 @@ attend_mfma_kernel(AttendArgs a) {
       ++tp;
     }
   }
+}
+
+// Split-mode merge: per (query, head, 4 channels), the partial outputs of the key ranges are
+// combined in the common scale of their largest running max.  Every range started from the
+// sink state (max = sink, sum = 1), so n_split - 1 copies of the sink term are removed.
+__global__ void __launch_bounds__(256) attend_merge_kernel(const float* __restrict__ part,
+                                                           const float* __restrict__ sink,
+                                                           bf16_t* __restrict__ out, int n_q,
+                                                           int n_split) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid >= n_q * AH * (AD / 4)) return;
+  const int q = gid / (AH * (AD / 4));
+  const int h = (gid / (AD / 4)) % AH;
+  const int c = (gid % (AD / 4)) * 4;
+  const float* ml = part + static_cast<size_t>(n_q) * n_split * AH * AD;
+  float mx = -INFINITY;
+  for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, ml[((q * n_split + i) * AH + h) * 2]);
+  const float sink2 = sink[h] * kLog2e;
+  float l = -static_cast<float>(n_split - 1) * __builtin_amdgcn_exp2f(sink2 - mx);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < n_split; ++i) {
+    const size_t item = static_cast<size_t>(q) * n_split + i;
+    const float w = __builtin_amdgcn_exp2f(ml[(item * AH + h) * 2] - mx);
+    l += w * ml[(item * AH + h) * 2 + 1];
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + (item * AH + h) * AD + c);
+    acc += w * v;
+  }
+  const float inv = 1.f / l;
+  u32x2_t pk;
+  pk[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2_t*>(out + (static_cast<size_t>(q) * AH + h) * AD + c) = pk;
+}
+
+static int device_cus() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      n_cu = n > 0 ? n : 1;
+    else
+      return 1;
+  }
+  return n_cu;
+}
+
+constexpr int kMaxSplit = 8;
+
+int attend_split_count(int n_q) {
+  if (n_q <= 0) return 1;
+  const int n = device_cus() / n_q;
+  return n < 2 ? 1 : (n > kMaxSplit ? kMaxSplit : n);
+}
+
+size_t attend_split_bytes(int n_q) {
+  const int ns = attend_split_count(n_q);
+  if (ns < 2) return 0;
+  return static_cast<size_t>(n_q) * ns * (AH * AD + AH * 2) * sizeof(float);
 }
 
 bool attend_fast(int H, int D, int r, int dtype) {
@@ -630,8 +754,16 @@ static hipError_t launch_mfma(const AttendArgs& a, hipStream_t st) {
     attr_set = true;
   }
   const int n_q = a.B * a.T;
-  const unsigned blocks = static_cast<unsigned>(n_q < n_cu ? n_q : n_cu);
+  const int n_items = n_q * a.n_split;
+  const unsigned blocks = static_cast<unsigned>(n_items < n_cu ? n_items : n_cu);
   hipLaunchKernelGGL((attend_mfma_kernel<CSA, R>), dim3(blocks), dim3(576), kLdsBytes, st, a);
+  if (a.n_split > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int total = n_q * AH * (AD / 4);
+    hipLaunchKernelGGL(attend_merge_kernel, dim3((total + 255) / 256), dim3(256), 0, st, a.part,
+                       a.sink, static_cast<bf16_t*>(a.out), n_q, a.n_split);
+  }
   return hipGetLastError();
 }
 

@@ -44,7 +44,17 @@ struct AttendArgs {
   int dtype;
   bool csa;
   double inv_freq[128];  // theta^(-2i/r), i < r/2, formed on the host in double precision
+  // Split mode (few queries): each query's keys are cut into n_split ranges scored by separate
+  // workgroups; part holds their fp32 partial outputs [items][H][D] then (max, sum) pairs
+  // [items][H][2], merged by a second kernel.  n_split = 1: part unused.
+  int n_split;
+  float* part;
 };
+
+// Key ranges per query the split mode uses for n_q queries on this device (1: no split), and
+// the workspace it needs.
+int attend_split_count(int n_q);
+size_t attend_split_bytes(int n_q);
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 

@@ -15,8 +15,8 @@ from typing import Dict, Optional
 
 import torch
 
-from . import (csa_attend, csa_compress, csa_index_topk, csa_index_topk_workspace_size,
-               hca_attend, swa_concat)
+from . import (attend_workspace_size, csa_attend, csa_compress, csa_index_topk,
+               csa_index_topk_workspace_size, hca_attend, swa_concat)
 
 
 @dataclasses.dataclass
@@ -221,6 +221,8 @@ class DecodeState:
         self.topk_idx = torch.empty(self.B, 1, self.k_eff, dtype=torch.int32, device=dev)
         ws = csa_index_topk_workspace_size(self.B, 1, N_cap, self.k_eff)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        aw = attend_workspace_size(self.B, 1, sh.H, sh.D)  # key-range split of few queries
+        self.attend_ws = torch.empty(aw, dtype=torch.uint8, device=dev) if aw > 0 else None
         self.out = torch.empty(self.B, 1, sh.H, sh.D, dtype=sh.dtype, device=dev)
 
 
@@ -230,5 +232,5 @@ def csa_decode_step(st: DecodeState, stream=None) -> torch.Tensor:
     csa_index_topk(t["q_idx"], t["w_idx"], t["k_pool"], st.q_pos0, st.n_pool, st.topk_idx, None,
                    sh.m, st.workspace, stream=stream)
     csa_attend(t["q"], t["window"], st.kv_pos0, t["pool"], st.topk_idx, t["sink"], st.q_pos0,
-               st.out, sh.W, sh.r, sh.base, stream=stream)
+               st.out, sh.W, sh.r, sh.base, workspace=st.attend_ws, stream=stream)
     return st.out

@@ -48,6 +48,9 @@ def test_workspace_size(lib):
     assert lib.csa_index_topk_workspace_size(1, 8192, 2048, 512) == 8192 * 2048 * 4
     assert lib.csa_index_topk_workspace_size(3, 5, 7, 1) == 3 * 5 * 7 * 4
     assert lib.csa_index_topk_workspace_size(0, 5, 7, 1) == 0
+    # the split attention path exists only for the 64 x 512 bf16 shape
+    assert lib.attend_workspace_size(1, 1, 8, 64) == 0
+    assert lib.attend_workspace_size(0, 1, 64, 512) == 0
 
 
 def _compress(lib, **kw):
@@ -101,7 +104,7 @@ def test_attend_argument_errors(lib):
         a.update(kw)
         return lib.csa_attend(None, None, None, a["S_kv"], None, a["N"], None, a["k"], None,
                               None, None, a["B"], a["T"], a["H"], a["D"], a["W"], a["r"],
-                              a["theta"], 0, 0.0, a["dtype"], None)
+                              a["theta"], 0, 0.0, None, 0, a["dtype"], None)
     assert csa(k=0) == INVALID
     assert csa(k=5000) == UNSUPPORTED
     assert csa(W=0) == INVALID
@@ -115,7 +118,7 @@ def test_attend_argument_errors(lib):
         a = dict(m=128, B=1, T=4)
         a.update(kw)
         return lib.hca_attend(None, None, None, 128, None, 512, None, a["m"], None, None, None,
-                              a["B"], a["T"], 64, 512, 128, 64, 1e4, 0, 0.0, BF16, None)
+                              a["B"], a["T"], 64, 512, 128, 64, 1e4, 0, 0.0, None, 0, BF16, None)
     assert hca(m=0) == INVALID
     assert hca(T=0) == OK
     assert hca() == INVALID

@@ -185,7 +185,7 @@ def test_index_topk_exact_ties():
 # ---------------------------------------------------------------------------- attention
 
 def _attend_case(dt, csa, B, T, H, D, r, Wn, S_kv, kv_pos0, q_pos0, N_cap, k=0, n_pool=None,
-                 m_hca=16, seed=20, shuffle_invalid=False):
+                 m_hca=16, seed=20, shuffle_invalid=False, split=False):
     q = normal("q", (B, T, H, D), seed)
     win = normal("win", (B, S_kv, D), seed)
     pool = normal("pool", (B, max(N_cap, 1), D), seed)[:, :N_cap]
@@ -194,16 +194,21 @@ def _attend_case(dt, csa, B, T, H, D, r, Wn, S_kv, kv_pos0, q_pos0, N_cap, k=0, 
     base, off = 10000.0, 11
     out = torch.empty(B, T, H, D, dtype=torch_dtype(dt), device="cuda")
     pool_t = dev(ps) if N_cap > 0 else None
+    wsp = None
+    if split:  # key ranges of each query on separate workgroups, merged afterwards
+        nb = L.attend_workspace_size(B, T, H, D)
+        assert nb > 0, "the split path should apply to this few queries"
+        wsp = torch.empty(nb, dtype=torch.uint8, device="cuda")
     if csa:
         topk = W.random_index_lists(seed, "topk", B, T, k, N_cap, shuffle_invalid)
         L.csa_attend(dev(qs), dev(ws_), i32(kv_pos0), pool_t, dev(topk), dev(sink), i32(q_pos0),
-                     out, Wn, r, base, off)
+                     out, Wn, r, base, off, workspace=wsp)
         ref = oracle.csa_attend(W.to_f64(qs), W.to_f64(ws_), kv_pos0, W.to_f64(ps), topk, sink,
                                 q_pos0, Wn, r, base, off)
     else:
         L.hca_attend(dev(qs), dev(ws_), i32(kv_pos0), pool_t,
                      i32(n_pool) if n_pool is not None else None, m_hca, dev(sink), i32(q_pos0),
-                     out, Wn, r, base, off)
+                     out, Wn, r, base, off, workspace=wsp)
         ref = oracle.hca_attend(W.to_f64(qs), W.to_f64(ws_), kv_pos0,
                                 W.to_f64(ps) if N_cap > 0 else None,
                                 n_pool if n_pool is not None else ([N_cap] * B if N_cap else None),
@@ -249,6 +254,27 @@ def test_decode_shaped_attend():
     L_b = [5000, 70000, 129, 20000]
     _attend_case("bf16", True, B, 1, 64, 512, 64, Wn, Wn, [x - Wn for x in L_b],
                  [x - 1 for x in L_b], 500, k=512, seed=28)
+
+
+def test_decode_shaped_attend_split():
+    # the same with each query's keys cut into ranges on separate workgroups and merged
+    B, Wn = 4, 128
+    L_b = [5000, 70000, 129, 20000]
+    _attend_case("bf16", True, B, 1, 64, 512, 64, Wn, Wn, [x - Wn for x in L_b],
+                 [x - 1 for x in L_b], 500, k=512, seed=28, split=True)
+
+
+def test_split_attend_short_and_empty_queries():
+    # HCA, one query per sequence: a long one, one with fewer tiles than ranges (empty ranges
+    # run a masked tile), one whose window rows all lie outside the buffer and whose pool is
+    # empty (the sink alone: output 0)
+    _attend_case("bf16", False, 3, 1, 64, 512, 64, 128, 128, [3000, 40, 500], [3127, 60, 300],
+                 600, n_pool=[600, 2, 0], m_hca=8, seed=29, split=True)
+
+
+def test_split_attend_csa_two_queries_per_sequence():
+    _attend_case("bf16", True, 3, 2, 64, 512, 64, 128, 256, [0, 100, 7], [200, 300, 40], 300,
+                 k=128, seed=30, split=True, shuffle_invalid=True)
 
 
 # ---------------------------------------------------------------------------- errors
