@@ -256,43 +256,48 @@ __global__ void __launch_bounds__(256) index_score_stream(
     for (int e = 0; e < 16; ++e) wv[hb][e] = wp[(e >> 2) * 8 + (e & 3)];
   }
 
-  // rows past e1 are clamped to e1 - 1 (a visible row): loads stay in bounds, results unused
+  // rows past e1 are clamped to e1 - 1 (a visible row): loads stay in bounds, results unused.
+  // Three register sets rotate: sub-tiles n0 + 32 and n0 + 64 are in flight while n0 is
+  // scored (two sub-tiles of prefetch per wave).
   const bf16_t* kb = k_pool + static_cast<size_t>(b) * N_cap * IX_CI + half * 8;
-  uint4 cur[IX_CI / 16], nxt[IX_CI / 16];
-  {
-    const bf16_t* kr = kb + static_cast<size_t>(min(e0 + l32, e1 - 1)) * IX_CI;
-#pragma unroll
-    for (int ks = 0; ks < IX_CI / 16; ++ks) cur[ks] = *reinterpret_cast<const uint4*>(kr + ks * 16);
-  }
   float* srow = scores + qrow * N_cap;
-  for (int n0 = e0; n0 < e1; n0 += 32) {
-    if (n0 + 32 < e1) {  // wave-uniform
-      const bf16_t* kr = kb + static_cast<size_t>(min(n0 + 32 + l32, e1 - 1)) * IX_CI;
+  auto load = [&](uint4 (&dst)[IX_CI / 16], int n) {
+    const bf16_t* kr = kb + static_cast<size_t>(min(n + l32, e1 - 1)) * IX_CI;
 #pragma unroll
-      for (int ks = 0; ks < IX_CI / 16; ++ks) nxt[ks] = *reinterpret_cast<const uint4*>(kr + ks * 16);
-    }
+    for (int ks = 0; ks < IX_CI / 16; ++ks) dst[ks] = *reinterpret_cast<const uint4*>(kr + ks * 16);
+  };
+  auto score = [&](const uint4 (&src)[IX_CI / 16], int n0) {
     f32x16_t acc[2];
+    const f32x16_t zero = {};
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
+      acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][0], as_bf16x8(src[0]), zero, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[hb][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < IX_CI / 16; ++ks) {
-      const bf16x8_t bk = as_bf16x8(cur[ks]);
+    for (int ks = 1; ks < IX_CI / 16; ++ks)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
-        acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][ks], bk, acc[hb], 0, 0, 0);
+        acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[hb][ks], as_bf16x8(src[ks]), acc[hb], 0, 0, 0);
+    // ReLU as an integer max: non-negative floats are non-negative integers, and -0 -> +0
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p0 += wv[0][e] * __int_as_float(max(__float_as_int(acc[0][e]), 0));
+      p1 += wv[1][e] * __int_as_float(max(__float_as_int(acc[1][e]), 0));
     }
-    float part = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) part += wv[hb][e] * fmaxf(acc[hb][e], 0.f);
-    part = xhalf_sum(part);
+    const float part = xhalf_sum(p0 + p1);
     const int n = n0 + l32;
     if (half == 0 && n < e1) srow[n] = part;
-#pragma unroll
-    for (int ks = 0; ks < IX_CI / 16; ++ks) cur[ks] = nxt[ks];
+  };
+  uint4 b0[IX_CI / 16], b1[IX_CI / 16], b2[IX_CI / 16];
+  load(b0, e0);
+  if (e0 + 32 < e1) load(b1, e0 + 32);
+  for (int n0 = e0; n0 < e1; n0 += 96) {  // wave-uniform bounds throughout
+    if (n0 + 64 < e1) load(b2, n0 + 64);
+    score(b0, n0);
+    if (n0 + 96 < e1) load(b0, n0 + 96);
+    if (n0 + 32 < e1) score(b1, n0 + 32);
+    if (n0 + 128 < e1) load(b1, n0 + 128);
+    if (n0 + 64 < e1) score(b2, n0 + 64);
   }
 }
 
@@ -460,7 +465,9 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
     key[j] = (j < n_strides && i < V) ? score_key(s[i]) : 0u;
   }
 
-  const int n_inv = KPT * NT - min(V, KPT * NT);
+  // strides past the row are skipped (block-uniform); the last one may hold empty slots
+  const int n_reg = min(n_strides, KPT);
+  const int n_inv = n_reg * NT - min(V, n_reg * NT);
   for (int i = tid; i < NW * 16 * 64; i += NT) (&hist[0][0][0])[i] = 0;
   __syncthreads();
 
@@ -472,8 +479,9 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
     // branch-free: a key outside the prefix adds 0
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      atomicAdd(hcol + ((key[j] >> shift) & 15u) * 64,
-                static_cast<uint32_t>((key[j] & mask) == prefix));
+      if (j < n_reg)
+        atomicAdd(hcol + ((key[j] >> shift) & 15u) * 64,
+                  static_cast<uint32_t>((key[j] & mask) == prefix));
     for (int j = KPT; j < n_strides; ++j) {
       const int i = j * NT + tid;
       if (i >= V) break;
@@ -645,7 +653,8 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
     const int i = j * 64 + lane;
     key[j] = (j < n_str && i < V) ? score_key(s[i]) : 0u;
   }
-  const int n_inv = KPL * 64 - min(V, KPL * 64);
+  const int n_reg = min(n_str, KPL);  // register strides in use (wave-uniform)
+  const int n_inv = n_reg * 64 - min(V, n_reg * 64);
 
   uint32_t* hc = &hist[wave][0][lane];
 #pragma unroll
@@ -660,8 +669,9 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
     const int shift = 28 - 4 * pass;
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
-      atomicAdd(hc + ((key[j] >> shift) & 15u) * 64,
-                static_cast<uint32_t>((key[j] & mask) == prefix));
+      if (j < n_reg)
+        atomicAdd(hc + ((key[j] >> shift) & 15u) * 64,
+                  static_cast<uint32_t>((key[j] & mask) == prefix));
     for (int j = KPL; j < n_str; ++j) {
       const int i = j * 64 + lane;
       if (i < V) {
