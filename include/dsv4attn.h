@@ -86,6 +86,32 @@ int csa_compress(const void* x, const void* gate, const float* bias, void* pool,
                  void* stream);
 
 /*
+ * compressor_cache_update - one decode step of a compressor cache ("Cache layers": the HCA
+ * cache's compressor buffer / pool / count, the CSA cache's compressor with its overlap
+ * state and the parallel indexer's buffer / pool / count / overlap at index_head_dim).
+ *
+ * Sequence b has L = lengths[b] tokens including the new one (L >= 1; L < 1: untouched).
+ * Its raw token ring x_ring[b] / gate_ring[b] holds the last span tokens, span = 2m with
+ * overlap (CSA) or m (HCA): token position p lives in slot p mod span.  The call stores the
+ * new token (x_new[b], gate_new[b]) in slot (L-1) mod span; when emit != 0 and L mod m == 0
+ * the token closes entry w = L/m - 1, which is pooled from the ring exactly as csa_compress
+ * defines it (same window, bias and RoPE at (w+1)m - 1 + rope_pos_offset) and written to
+ * pool[b, w] (entries w >= N_cap are not written).  emit = 0 only fills the ring (e.g. with
+ * the last span tokens of a prefill whose entries are already pooled).
+ *
+ *   x_new, gate_new : [B, C] dtype.  x_ring, gate_ring : [B, span, C] dtype (caller-owned
+ *   state, kept across calls).  bias : [span, C] float32 or NULL.  pool : [B, N_cap, C].
+ *   lengths : [B] int32 device array.  C, rope_dim and alignment as for csa_compress;
+ *   span <= 4096 (DSV4_ERR_UNSUPPORTED otherwise).  Sequences are independent; one call
+ *   per layer and per compressor (the CSA K=V pool and its indexer keys are two calls).
+ */
+int compressor_cache_update(const void* x_new, const void* gate_new, void* x_ring,
+                            void* gate_ring, const float* bias, void* pool, const int* lengths,
+                            int B, int C, int m, int overlap, int N_cap, int rope_dim,
+                            double rope_theta, long long rope_pos_offset, int emit, int dtype,
+                            void* stream);
+
+/*
  * csa_index_topk - Lightning Indexer scores and top-k per query ("Hybrid attention (§2.3)",
  * CSA item, eqs. 13-17; "Attention mask layout", CSA paragraph for the -1 sentinel;
  * "DeepseekV4Config": index_n_heads, index_head_dim, index_topk).

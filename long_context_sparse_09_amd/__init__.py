@@ -82,6 +82,19 @@ def csa_compress(x, gate, bias, pool, m: int, overlap: bool, entry_begin: int = 
         _stream(stream)))
 
 
+def compressor_cache_update(x_new, gate_new, x_ring, gate_ring, bias, pool, lengths, m: int,
+                            overlap: bool, rope_dim: int = 0, rope_theta: float = 10000.0,
+                            rope_pos_offset: int = 0, emit: bool = True, stream=None) -> None:
+    """x_new, gate_new [B,C]; x_ring, gate_ring [B,span,C]; bias [span,C] fp32 or None;
+    pool [B,N_cap,C] (or None when emit is False); lengths [B] int32 (tokens incl. the new)."""
+    B, C = x_new.shape
+    N_cap = 0 if pool is None else pool.shape[1]
+    _check("compressor_cache_update", lib().compressor_cache_update(
+        _ptr(x_new), _ptr(gate_new), _ptr(x_ring), _ptr(gate_ring), _ptr(bias), _ptr(pool),
+        _ptr(lengths), B, C, m, int(bool(overlap)), N_cap, rope_dim, float(rope_theta),
+        int(rope_pos_offset), int(bool(emit)), _dtype(x_new), _stream(stream)))
+
+
 def csa_index_topk_workspace_size(B: int, T: int, N_cap: int, k: int) -> int:
     return int(lib().csa_index_topk_workspace_size(B, T, N_cap, k))
 

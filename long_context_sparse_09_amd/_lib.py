@@ -20,6 +20,9 @@ SIGNATURES = {
     "dsv4_last_error": ([], c_char_p),
     "csa_compress": ([c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                       c_int, c_int, c_int, c_int, c_double, c_ll, c_int, c_void_p], c_int),
+    "compressor_cache_update": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_double,
+                                 c_ll, c_int, c_int, c_void_p], c_int),
     "csa_index_topk_workspace_size": ([c_int, c_int, c_int, c_int], c_size_t),
     "csa_index_topk": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_size_t,

@@ -91,6 +91,33 @@ int csa_compress(const void* x, const void* gate, const float* bias, void* pool,
                   "csa_compress");
 }
 
+int compressor_cache_update(const void* x_new, const void* gate_new, void* x_ring,
+                            void* gate_ring, const float* bias, void* pool, const int* lengths,
+                            int B, int C, int m, int overlap, int N_cap, int rope_dim,
+                            double rope_theta, long long rope_pos_offset, int emit, int dtype,
+                            void* stream) {
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(B >= 0 && N_cap >= 0, "negative size");
+  REQUIRE(m >= 1, "m must be >= 1");
+  REQUIRE(overlap == 0 || overlap == 1, "overlap must be 0 or 1");
+  REQUIRE(C >= 2 && C % 2 == 0, "C must be even and >= 2");
+  if (!(C % 8 == 0 ? C <= 2048 : C <= 512))
+    return fail(DSV4_ERR_UNSUPPORTED, "C=%d: need C <= 2048 (multiple of 8) or <= 512", C);
+  if ((overlap ? 2 * m : m) > 4096) return fail(DSV4_ERR_UNSUPPORTED, "window span above 4096");
+  if (int rc = check_rope(rope_dim, C, rope_theta)) return rc;
+  if (B == 0) return ok();
+  REQUIRE(x_new && gate_new && x_ring && gate_ring && lengths, "null required pointer");
+  REQUIRE(!emit || pool, "pool required when emitting entries");
+  REQUIRE(aligned16(x_new) && aligned16(gate_new) && aligned16(x_ring) && aligned16(gate_ring) &&
+              (!pool || aligned16(pool)) && (!bias || aligned16(bias)),
+          "pointers must be 16-byte aligned");
+  return launched(dsv4::launch_cache_update(x_new, gate_new, x_ring, gate_ring, bias, pool,
+                                            lengths, B, C, m, overlap, N_cap, rope_dim,
+                                            rope_theta, rope_pos_offset, emit, dtype,
+                                            static_cast<hipStream_t>(stream)),
+                  "compressor_cache_update");
+}
+
 size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int k) {
   (void)k;
   if (B <= 0 || T <= 0 || N_cap <= 0) return 0;

@@ -157,6 +157,107 @@ hipError_t launch_compress(const void* x, const void* gate, const float* bias, v
 }
 
 // ---------------------------------------------------------------------------
+// Compressor cache update (decode): one workgroup per sequence.  lengths[b] = L counts the
+// sequence's tokens including the new one.  The new raw token (x_new[b], gate_new[b]) goes
+// into ring slot (L-1) mod span of the sequence's token ring (span = 2m with overlap, m
+// without); when it closes an entry (L mod m == 0, emit != 0), entry w = L/m - 1 is pooled
+// from the ring exactly as compress_kernel pools it with P = 1 (same slot order, same
+// online softmax) and rotated at (w+1)m - 1.  Each thread owns one channel chunk of both the
+// store and the pooling, so it reads back its own write.
+// ---------------------------------------------------------------------------
+template <typename T, int VEC>
+__global__ void __launch_bounds__(256) cache_update_kernel(
+    const T* __restrict__ x_new, const T* __restrict__ g_new, T* x_ring, T* g_ring,
+    const float* __restrict__ bias, T* __restrict__ pool, const int* __restrict__ lengths, int C,
+    int m, int overlap, int N_cap, int r, const RopeFreq rf, long long pos_off, int emit) {
+  __shared__ double inv_freq[kMaxRope / 2];
+  for (int i = threadIdx.x; i < r / 2; i += blockDim.x) inv_freq[i] = rf.inv[i];
+  __syncthreads();
+  const int b = blockIdx.x;
+  const int L = lengths[b];
+  if (L < 1) return;  // block-uniform; no barrier follows
+  const int span = overlap ? 2 * m : m;
+  const int G = C / VEC;
+  const size_t ring0 = static_cast<size_t>(b) * span;
+  const int slot = (L - 1) % span;
+  const bool closes = emit && (L % m) == 0 && (L / m - 1) < N_cap;
+  const int w = L / m - 1;
+  const int lo = overlap ? (w - 1) * m : w * m;
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int c0 = g * VEC;
+    float v[VEC];
+    Chunk<T>::template load<VEC>(x_new + static_cast<size_t>(b) * C + c0, v);
+    Chunk<T>::template store<VEC>(x_ring + (ring0 + slot) * C + c0, v);
+    Chunk<T>::template load<VEC>(g_new + static_cast<size_t>(b) * C + c0, v);
+    Chunk<T>::template store<VEC>(g_ring + (ring0 + slot) * C + c0, v);
+    if (!closes) continue;
+    float mx[VEC], sm[VEC], acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) { mx[i] = -INFINITY; sm[i] = 0.f; acc[i] = 0.f; }
+    for (int s = 0; s < span; ++s) {
+      const int p = lo + s;  // token position; absent before 0
+      if (p < 0) continue;
+      const size_t row = ring0 + p % span;
+      float xv[VEC], gv[VEC];
+      Chunk<T>::template load<VEC>(x_ring + row * C + c0, xv);
+      Chunk<T>::template load<VEC>(g_ring + row * C + c0, gv);
+      if (bias != nullptr) {
+        float bv[VEC];
+        Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s) * C + c0, bv);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) gv[i] += bv[i];
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float a = gv[i] * kLog2e;
+        const float d = exp2f(-fabsf(a - mx[i]));
+        if (a > mx[i]) {
+          sm[i] = sm[i] * d + 1.f;
+          acc[i] = acc[i] * d + xv[i];
+          mx[i] = a;
+        } else {
+          sm[i] += d;
+          acc[i] += d * xv[i];
+        }
+      }
+    }
+    float out[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) out[i] = acc[i] / sm[i];
+    const double pos = static_cast<double>((static_cast<long long>(w) + 1) * m - 1 + pos_off);
+    rope_chunk<VEC, sizeof(T) == 2>(out, c0, C, r, pos, inv_freq);
+    Chunk<T>::template store<VEC>(pool + (static_cast<size_t>(b) * N_cap + w) * C + c0, out);
+  }
+}
+
+template <typename T, int VEC>
+static hipError_t cache_update_t(const void* x_new, const void* g_new, void* x_ring, void* g_ring,
+                                 const float* bias, void* pool, const int* lengths, int B, int C,
+                                 int m, int overlap, int N_cap, int r, double theta, long long off,
+                                 int emit, hipStream_t st) {
+  const int G = C / VEC;
+  const int threads = G >= 256 ? 256 : ((G + 63) / 64) * 64;
+  hipLaunchKernelGGL((cache_update_kernel<T, VEC>), dim3(B), dim3(threads), 0, st,
+                     static_cast<const T*>(x_new), static_cast<const T*>(g_new),
+                     static_cast<T*>(x_ring), static_cast<T*>(g_ring), bias, static_cast<T*>(pool),
+                     lengths, C, m, overlap, N_cap, r, make_rope_freq(r, theta), off, emit);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_update(const void* x_new, const void* g_new, void* x_ring, void* g_ring,
+                               const float* bias, void* pool, const int* lengths, int B, int C,
+                               int m, int overlap, int N_cap, int r, double theta, long long off,
+                               int emit, int dtype, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const bool v8 = (C % 8 == 0) && (C / 8 <= 256);
+  if (dtype == 1)
+    return v8 ? cache_update_t<bf16_t, 8>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st)
+              : cache_update_t<bf16_t, 2>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st);
+  return v8 ? cache_update_t<float, 8>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st)
+            : cache_update_t<float, 2>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st);
+}
+
+// ---------------------------------------------------------------------------
 // swa_concat: rotate raw K=V rows at their positions into the window buffer.
 //
 // The chunks of a row that hold no rotary channel (the first Gn of its G VEC-channel chunks)

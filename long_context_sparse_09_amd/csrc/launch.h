@@ -10,6 +10,11 @@ hipError_t launch_compress(const void* x, const void* gate, const float* bias, v
                            int S, int C, int m, int overlap, int e0, int e1, int N_cap, int r,
                            double theta, long long off, int dtype, hipStream_t st);
 
+hipError_t launch_cache_update(const void* x_new, const void* g_new, void* x_ring, void* g_ring,
+                               const float* bias, void* pool, const int* lengths, int B, int C,
+                               int m, int overlap, int N_cap, int r, double theta, long long off,
+                               int emit, int dtype, hipStream_t st);
+
 hipError_t launch_swa(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0,
                       int B, int S_new, int S_cap, int D, int r, double theta, long long off,
                       int dtype, hipStream_t st);

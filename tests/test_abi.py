@@ -134,3 +134,22 @@ def test_swa_argument_errors(lib):
     assert call(r=-2) == INVALID
     assert call(S_new=0) == OK
     assert call() == INVALID
+
+
+def test_cache_update_argument_errors(lib):
+    def call(**kw):
+        a = dict(B=2, C=512, m=4, overlap=1, N_cap=64, r=64, theta=1e4, emit=1, dtype=BF16)
+        a.update(kw)
+        return lib.compressor_cache_update(None, None, None, None, None, None, None, a["B"],
+                                           a["C"], a["m"], a["overlap"], a["N_cap"], a["r"],
+                                           a["theta"], 0, a["emit"], a["dtype"], None)
+    assert call(dtype=3) == INVALID
+    assert call(m=0) == INVALID
+    assert call(overlap=2) == INVALID
+    assert call(C=5) == INVALID
+    assert call(N_cap=-1) == INVALID
+    assert call(r=66, C=64) == INVALID                        # rope wider than a row
+    assert call(C=4096) == UNSUPPORTED
+    assert call(m=2049) == UNSUPPORTED                        # ring of 2m rows above 4096
+    assert call(B=0) == OK and lib.dsv4_last_error() == b""
+    assert call() == INVALID and b"null" in lib.dsv4_last_error()
