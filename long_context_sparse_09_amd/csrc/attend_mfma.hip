@@ -12,24 +12,26 @@
 // Work decomposition
 //   * Persistent workgroups (one per CU) walk their queries as one stream of 32-key tiles:
 //     the window rows of a query, then its selected (CSA) or visible (HCA) pool rows.
-//   * Nine wavefronts in three roles, pipelined by one tile:
-//       - gather (wave 8): moves each tile's 32 key rows (1 KB each) from global memory
-//         straight into LDS (global_load_lds), three tiles ahead, into a ring of four
-//         tile buffers.  A vector-memory issue stalls the issuing wave at the CU's fill rate,
-//         so every gather sits in this one wave;
-//       - score (waves 0..3, (hb, kh)): heads [32hb, 32hb+32), channels [256kh, 256kh+256).
-//         Partial S^T = K[:, ch kh] . Q^T[ch kh] on v_mfma_f32_32x32x16_bf16 (A = 32 key rows
-//         from LDS, B = its half of the rotated Q in registers); the two waves of a head block
-//         swap partials through LDS, run the same online softmax, and publish P (bf16) and
-//         the rescale factor of the running max for the tile;
-//       - value (waves 4..7, (hb, kh)): O^T[ch kh, heads hb] += V^T . P^T, with V^T read from
-//         the same row-major tile through ds_read_tr16_b64 (K = V is stored once) and P^T
-//         taken from LDS in exactly the B-operand layout the score waves produced it in.
+//   * Eight wavefronts in three roles, pipelined by one tile.  Waves w and w + 4 share a
+//     SIMD; the roles are placed so that every SIMD carries the same matrix work per tile:
+//       - gather (waves 4, 5: rows 0..15 and 16..31): move each tile's 32 key rows (1 KB
+//         each) from global memory straight into LDS (buffer_load ... lds, one row
+//         descriptor per row), three tiles ahead, into a ring of four tile buffers.  A
+//         vector-memory issue stalls the issuing wave at the CU's fill rate, so the gather
+//         sits in its own waves; for CSA they also copy the next query's index list into
+//         LDS while the current query's tiles stream, so a query switch waits on nothing;
+//       - score (waves 0, 1 = head block hb): heads [32hb, 32hb+32), all 512 channels.
+//         S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 key rows from LDS, B = the
+//         rotated Q in registers, 32 channel steps), then the online softmax of the tile;
+//         publishes P (bf16) and the rescale factor of the running max;
+//       - value (waves 2, 3, 6, 7 = (hb, kh)): O^T[ch kh, heads hb] += V^T . P^T over channels
+//         [256kh, 256kh+256), with V^T read from the same row-major tile through
+//         ds_read_tr16_b64 (K = V is stored once) and P^T taken from LDS in exactly the
+//         B-operand layout the score wave produced it in.
 //     In step s the score waves work on tile s+1, the value waves on tile s and the gather
-//     wave fills tile s+3; a score wave and a value wave share each SIMD, so one's matrix work
-//     covers the other's LDS and softmax latency.  Two workgroup barriers per step: X (tile
-//     s+1 landed, P(s) published, the buffer of tile s-1 free) and Y (partial logits
-//     exchanged).
+//     wave fills tile s+3.  Per tile each SIMD runs 32 matrix instructions: a score wave's
+//     32 (with a gather wave beside it) or two value waves' 16 each.  One workgroup
+//     barrier per step: tile s+1 landed, P(s) published, the buffer of tile s-1 free.
 //   * Online softmax in the log2 domain; the running max moves only when a logit exceeds it
 //     by 2^8 (lazy rescale).  The state starts from the sink: max = s_h, sum = 1, value 0.
 //   * RoPE angles are formed per lane in double precision (position x frequency, reduced to
@@ -61,13 +63,13 @@ constexpr int ANK = 32;                    // keys per tile
 constexpr int APITCH = AD * 2;             // LDS bytes per key row (swizzled, no pad)
 constexpr int ATILE = ANK * APITCH;        // bytes per tile buffer
 constexpr int NSLOT = 4;                   // tile ring
-constexpr int XS_OFF = NSLOT * ATILE;      // partial-logit exchange: [score wave][4][64] f32x4
-constexpr int P_OFF = XS_OFF + 4 * 4096;   // P tiles: [parity][hb][16-key half][64] bf16x8
+constexpr int P_OFF = NSLOT * ATILE;       // P tiles: [parity][hb][16-key half][64] bf16x8
 constexpr int AL_OFF = P_OFF + 2 * 2 * 2 * 64 * 16;  // rescale factors: [parity][64 heads]
 constexpr int LS_OFF = AL_OFF + 2 * 64 * 4;          // softmax sums at a query's end: [parity][64]
-constexpr int KL_OFF = LS_OFF + 2 * 64 * 4;          // gather wave's key list (CSA)
+constexpr int KL_OFF = LS_OFF + 2 * 64 * 4;          // gather waves' key lists (CSA) [parity]
 constexpr int kMaxTopk = 1024;                       // key-list capacity on this path
-constexpr int NK_OFF = KL_OFF + kMaxTopk * 4;        // key counts of queries [j % 8]
+constexpr int RL_OFF = KL_OFF + 2 * kMaxTopk * 4;    // raw index list of the next query [gather wave]
+constexpr int NK_OFF = RL_OFF + 2 * kMaxTopk * 4;    // key counts of queries [j % 8]
 constexpr int IF_OFF = NK_OFF + 8 * 4;               // RoPE frequencies (double) [32]
 constexpr int kLdsBytes = IF_OFF + 32 * 8;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
@@ -117,8 +119,8 @@ __device__ __forceinline__ void rope_pair(double pos, double inv_freq, float& c,
 
 // Workgroup barrier for LDS hand-offs.  __syncthreads() also drains every outstanding
 // vector-memory operation of the calling wave (its release fence waits for vmcnt 0), which
-// would make the gather wave wait for tiles it has only just issued; here only this wave's
-// LDS operations are drained.  The gather wave orders its tiles with explicit vmcnt waits.
+// would make a gather wave wait for tiles it has only just issued; here only this wave's
+// LDS operations are drained.  The gather waves order their tiles with explicit vmcnt waits.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
@@ -202,7 +204,7 @@ __device__ __forceinline__ void set_keys(QInfo& d, int n_cmp, int n_split) {
 }
 
 template <bool CSA, int R>  // R = rotary channels, 0 or 64 (compile-time: only those chunks move)
-__global__ void __attribute__((amdgpu_flat_work_group_size(576, 576), amdgpu_waves_per_eu(3, 3)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 attend_mfma_kernel(AttendArgs a) {
   static_assert(R == 0 || R == 64, "rotary width on this path");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -226,30 +228,47 @@ attend_mfma_kernel(AttendArgs a) {
   const int n_mine = (n_q - slot + G - 1) / G;
   auto qid_of = [&](int j) { return n_q - 1 - (j * G + slot); };
 
-  if (wave == 8) {
-    // ------------------------------------------------------------------ gather wave
+  if (wave == 4 || wave == 5) {
+    // ------------------------------------------------------------------ gather waves
+    // Wave 4 moves rows 0..15 of every tile, wave 5 rows 16..31; both walk the same cursor.
     __builtin_amdgcn_s_setprio(3);  // its issue slots go first: the other waves wait on its tiles
+    const int gh = wave - 4;
     const bf16_t* win0 = static_cast<const bf16_t*>(a.kv_win);
     const bf16_t* pool0 = static_cast<const bf16_t*>(a.pool);
-    int* kl = reinterpret_cast<int*>(lds + KL_OFF);
+    int* kl = reinterpret_cast<int*>(lds + KL_OFF);  // [query parity][kMaxTopk]
     int iq = 0, it = 0;  // issue cursor: query rank, tile
     QInfo qi;
     unsigned voff[16];  // lane offset of a row whose chunks are XOR-ed with j
 #pragma unroll
     for (int j = 0; j < 16; ++j) voff[j] = static_cast<unsigned>(lane ^ j) << 4;
+    // CSA: the raw index list of query j + 1 is copied into LDS (LDS-DMA) while query j is
+    // gathered, so that switching queries waits on no memory latency.  The copy of query
+    // j + 1 is issued before the tile loads of every later step, so once the loads of the
+    // current tile are the only ones allowed in flight (vmcnt(16)) it has landed.
+    constexpr int NC = kMaxTopk / 64;
+    const int* rl = reinterpret_cast<const int*>(lds + RL_OFF) + gh * kMaxTopk;
+    auto list_dma = [&](int j) {
+      const QInfo d = query_geom<CSA>(a, qid_of(j));
+      const rsrc_t idx_rs = make_rs(a.topk_idx + (static_cast<size_t>(d.b) * a.T + d.t) * a.k,
+                                    static_cast<unsigned>(a.k) * 4u);
+#pragma unroll
+      for (int c = 0; c < kMaxTopk / 256; ++c)  // 256 entries (1 KB) per instruction
+        if (c * 256 < a.k)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(idx_rs, (lds_void*)(rl + c * 256), 16,
+                                                   static_cast<unsigned>(c * 1024 + lane * 16), 0, 0, 0);
+    };
+    if constexpr (CSA) list_dma(0);
     auto load_query = [&](int j) {
       qi = query_geom<CSA>(a, qid_of(j));
       if constexpr (CSA) {  // compact the valid entries, in order
-        const rsrc_t idx_rs = make_rs(a.topk_idx + (static_cast<size_t>(qi.b) * a.T + qi.t) * a.k,
-                                      static_cast<unsigned>(a.k) * 4u);
-        // every load of the list first (one memory latency), then the ballot compaction
-        constexpr int NC = kMaxTopk / 64;
+        if (j == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0x4F70);         // vmcnt(16): all but this tile's loads
         int ld[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          ld[c] = c * 64 < a.k ? static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(
-                                     idx_rs, static_cast<unsigned>(c * 64 + lane) * 4u, 0, 0))
-                               : -1;
+        for (int c = 0; c < NC; ++c) ld[c] = c * 64 < a.k ? rl[c * 64 + lane] : -1;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read before the next copy lands
+        if (j + 1 < n_mine) list_dma(j + 1);
+        int* klq = kl + (j & 1) * kMaxTopk;
         int base = 0;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -260,7 +279,7 @@ attend_mfma_kernel(AttendArgs a) {
           const unsigned long long m = __ballot(v);
           const int pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
                                                            __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
-          if (v) kl[pos] = e;
+          if (v) klq[pos] = e;
           base += __popcll(m);
         }
         set_keys(qi, base, a.n_split);
@@ -275,7 +294,7 @@ attend_mfma_kernel(AttendArgs a) {
         if (x < qi.n_win) {
           row = win0 + (static_cast<size_t>(qi.b) * a.S_kv + qi.r0 + x) * AD;
         } else {
-          const int e = CSA ? kl[x - qi.n_win] : x - qi.n_win;
+          const int e = CSA ? kl[(iq & 1) * kMaxTopk + x - qi.n_win] : x - qi.n_win;
           row = pool0 + (static_cast<size_t>(qi.b) * a.N_cap + e) * AD;
         }
       } else {  // masked filler: the query's own first row (in bounds, finite)
@@ -292,11 +311,16 @@ attend_mfma_kernel(AttendArgs a) {
         const int r = h * 16 + i;
         const unsigned lo32 = __builtin_amdgcn_readlane(rlo, r);
         const unsigned hi32 = __builtin_amdgcn_readlane(rhi, r);
-        const unsigned char* src = reinterpret_cast<const unsigned char*>(
-            (static_cast<unsigned long long>(hi32) << 32) | lo32);
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + voff[swz(r)]),
-                                         (lds_void*)(tb + r * APITCH), 16, 0, 0);
+        void* src = reinterpret_cast<void*>((static_cast<unsigned long long>(hi32) << 32) | lo32);
+        const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(src, static_cast<short>(0), APITCH, kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tb + r * APITCH), 16, voff[swz(i)], 0, 0, 0);
       }
+    };
+    // this wave's rows, with the half a compile-time constant in each copy: the row address
+    // then stays a scalar base plus one lane offset (the fast form of the load)
+    auto issue_mine = [&](int sl) {
+      if (gh == 0) issue_half(0, sl);
+      else issue_half(1, sl);
     };
     int n_issued = 0;
     bool have = true;  // the issue cursor points at a tile
@@ -312,34 +336,27 @@ attend_mfma_kernel(AttendArgs a) {
     };
 
     load_query(0);
-    // prologue: tiles 0 and 1
+    // prologue: tiles 0 and 1 (16 row loads per tile from this wave)
     tile_addr();
-    issue_half(0, 0);
-    issue_half(1, 0);
+    issue_mine(0);
     advance();
     if (have) {
       tile_addr();
-      issue_half(0, 1);
-      issue_half(1, 1);
+      issue_mine(1);
       advance();
-      __builtin_amdgcn_s_waitcnt(0x8F70);  // vmcnt(32): tile 0 has landed
+      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): tile 0 has landed
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
     // step s: fill tile s + 3 (its buffer held tile s - 1), then wait for tile s + 2
     for (int s = -1;; ++s) {
       lds_barrier();  // X(s)
-      const bool issuing = have;
-      const int sl = n_issued % NSLOT;
-      if (issuing) {
+      if (have) {
+        const int sl = n_issued % NSLOT;
         tile_addr();
-        issue_half(0, sl);
-      }
-      lds_barrier();  // Y(s)
-      if (issuing) {
-        issue_half(1, sl);
+        issue_mine(sl);
         advance();
-        __builtin_amdgcn_s_waitcnt(0x8F70);  // vmcnt(32)
+        __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
       } else {
         __builtin_amdgcn_s_waitcnt(0);
       }
@@ -349,36 +366,36 @@ attend_mfma_kernel(AttendArgs a) {
   }
 
   const int half = lane >> 5, l32 = lane & 31;
-  const int role_w = wave & 3;
-  const int hb = role_w & 1, kh = role_w >> 1;
+  const bool scorer = wave < 2;
+  const int hb = wave & 1;                    // head block of a score or value wave
+  const int kh = scorer ? 0 : (wave >> 2);    // channel half of a value wave
   const int head = hb * 32 + l32;
-  constexpr int NKS = AD / 2 / 16;  // channel steps of QK^T per wave
-  constexpr int NDT = AD / 2 / 32;  // output channel tiles per wave
+  constexpr int NKS = AD / 16;      // channel steps of QK^T per score wave
+  constexpr int NDT = AD / 2 / 32;  // output channel tiles per value wave
   bf16x8_t* pbuf = reinterpret_cast<bf16x8_t*>(lds + P_OFF);  // [parity][hb][ss][64]
   float* alph = reinterpret_cast<float*>(lds + AL_OFF);        // [parity][64 heads]
   float* lsum = reinterpret_cast<float*>(lds + LS_OFF);        // [parity][64 heads]
 
-  if (wave < 4) {
+  if (scorer) {
     // ------------------------------------------------------------------ score waves
     const float c2 = a.scale * kLog2e;  // logits in the log2 domain
     const float sink2 = a.sink[head] * kLog2e;
-    // This wave's half of Q^T (B operand): head, channels kh*256 + ks*16 + half*8
+    // Q^T (B operand): head, channels ks*16 + half*8 .. + 7
     bf16x8_t qf[NKS];
-    const unsigned qvoff = static_cast<unsigned>((head * AD + kh * (AD / 2) + half * 8) * 2);
+    const unsigned qvoff = static_cast<unsigned>((head * AD + half * 8) * 2);
     auto load_q = [&](const QInfo& d) {
       const rsrc_t q_rs = make_rs(qbase + (static_cast<size_t>(d.b) * a.T + d.t) * AH * AD, AH * AD * 2);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qvoff + ks * 32, 0, kNT));
     };
-    // rotary channels 448..511 = the last R/16 chunks of the kh = 1 half; pair index
-    // (channel - (512 - R)) / 2
+    // rotary channels AD-R .. AD-1 = the last R/16 channel steps; pair index (channel - (AD-R))/2
     auto rotate_q = [&](const QInfo& d) {
-      if (R == 0 || kh == 0) return;
+      if (R == 0) return;
       const double pos = static_cast<double>(d.p + a.pos_off);
 #pragma unroll
       for (int ks = NKS - R / 16; ks < NKS; ++ks) {
-        const int pr0 = (ks * 16 - (AD / 2 - R)) >> 1;  // pair of this lane: pr0 + 4 half + i/2
+        const int pr0 = (ks * 16 - (AD - R)) >> 1;  // pair of this lane: pr0 + 4 half + i/2
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           // both candidates at fixed offsets: scalar loads, no vector-memory wait
@@ -391,11 +408,9 @@ attend_mfma_kernel(AttendArgs a) {
         }
       }
     };
-    // QK^T A operand of step ks: row l32, chunk kh*32 + 2ks + half, at byte
-    // qk_base ^ (32 ks) (the chunk's low 4 bits are XOR-ed with swz(l32))
-    const int qk_base = l32 * APITCH + kh * (AD / 2) * 2 + ((half ^ swz(l32)) << 4);
-    f32x4_t* xme = reinterpret_cast<f32x4_t*>(lds + XS_OFF) + role_w * 256 + lane;
-    const f32x4_t* xpa = reinterpret_cast<const f32x4_t*>(lds + XS_OFF) + (role_w ^ 2) * 256 + lane;
+    // QK^T A operand of step ks: row l32, chunk 2ks + half, at byte qk_base ^ (32 ks) (the
+    // chunk's low 4 bits are XOR-ed with swz(l32))
+    const int qk_base = l32 * APITCH + ((half ^ swz(l32)) << 4);
 
     int jq = 0, tq = 0;  // cursor: query rank, tile within it
     QInfo cq = query_geom<CSA>(a, qid_of(0));
@@ -404,48 +419,30 @@ attend_mfma_kernel(AttendArgs a) {
     f32x16_t sacc;
     for (int s = -1;; ++s) {
       lds_barrier();  // X(s): tile s + 1 has landed
-      const bool has = jq < n_mine;  // this step scores tile s + 1
-      const bool first = has && tq == 0;
-      bool last = false;
-      if (has) {
-        if (first) {
-          if constexpr (CSA) set_keys(cq, __builtin_amdgcn_readfirstlane(nk[jq & 7]), a.n_split);
-          rotate_q(cq);
-          m_run = sink2;
-          l_run = 1.f;
-        }
-        last = (tq + 1 == cq.n_tiles);
-        const unsigned char* tb = lds + ((s + 1) % NSLOT) * ATILE;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-        constexpr int PF = 6;  // K fragments in flight
-        bf16x8_t kr[PF];
-#pragma unroll
-        for (int i = 0; i < PF; ++i) kr[i] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * i)));
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8_t kf = kr[ks % PF];
-          if (ks + PF < NKS)
-            kr[ks % PF] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * (ks + PF))));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (last && jq + 1 < n_mine) load_q(query_geom<CSA>(a, qid_of(jq + 1)));  // next Q streams in
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          xme[q4 * 64] = f32x4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
+      if (jq >= n_mine) break;  // this step would score tile s + 1
+      if (tq == 0) {
+        if constexpr (CSA) set_keys(cq, __builtin_amdgcn_readfirstlane(nk[jq & 7]), a.n_split);
+        rotate_q(cq);
+        m_run = sink2;
+        l_run = 1.f;
       }
-      lds_barrier();  // Y(s): partials exchanged
-      if (!has) break;
-      {
-        f32x4_t pv4[4];
+      const bool last = (tq + 1 == cq.n_tiles);
+      const unsigned char* tb = lds + ((s + 1) % NSLOT) * ATILE;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) pv4[q4] = xpa[q4 * 64];
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+      constexpr int PF = 6;  // K fragments in flight
+      bf16x8_t kr[PF];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
+      for (int i = 0; i < PF; ++i) kr[i] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * i)));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sacc[4 * q4 + i] += pv4[q4][i];
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8_t kf = kr[ks % PF];
+        if (ks + PF < NKS)
+          kr[ks % PF] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * (ks + PF))));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (last && jq + 1 < n_mine) load_q(query_geom<CSA>(a, qid_of(jq + 1)));  // next Q streams in
       // online softmax over the tile's 32 keys (lane: head l32, keys (e/4)*8 + half*4 + e%4)
       const int kbase = (cq.tb + tq) * ANK + half * 4;
       float tmax = -INFINITY;
@@ -467,23 +464,25 @@ attend_mfma_kernel(AttendArgs a) {
       const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float psum = 0.f;
-      bf16x8_t pb;  // this wave publishes keys 16kh .. 16kh + 15 of the tile
+      bf16x8_t pb0, pb1;  // keys 0..15 and 16..31 of the tile
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pv = __builtin_amdgcn_exp2f(sacc[e] - m_new);
         psum += pv;
-        if ((e >> 3) == kh) pb[e & 7] = static_cast<__bf16>(pv);
+        if (e < 8) pb0[e] = static_cast<__bf16>(pv);
+        else pb1[e - 8] = static_cast<__bf16>(pv);
       }
       psum = xhalf_sum(psum);
       l_run = l_run * alpha + psum;
       m_run = m_new;
       const int par = (s + 1) & 1;
-      pbuf[((par * 2 + hb) * 2 + kh) * 64 + lane] = pb;
+      pbuf[((par * 2 + hb) * 2 + 0) * 64 + lane] = pb0;
+      pbuf[((par * 2 + hb) * 2 + 1) * 64 + lane] = pb1;
       if (half == 0) {
-        if (kh == 0) alph[par * 64 + head] = alpha;
-        else if (last) lsum[par * 64 + head] = l_run;
+        alph[par * 64 + head] = alpha;
+        if (last) lsum[par * 64 + head] = l_run;
       }
-      if (a.n_split > 1 && last && half == 0 && kh == 1) {
+      if (a.n_split > 1 && last && half == 0) {
         // split mode: this key range's running max and sum (log2 domain, sink included)
         float* ml = a.part + static_cast<size_t>(n_q) * AH * AD + (static_cast<size_t>(qid_of(jq)) * AH + head) * 2;
         ml[0] = m_run;
@@ -518,7 +517,7 @@ attend_mfma_kernel(AttendArgs a) {
   QInfo cp = query_geom<CSA>(a, qid_of(0));
   bf16x8_t pb[2];
   // PV runs as one stream of 16 steps st = 16-key half * NDT + dt, whose V fragments are
-  // read VPF steps ahead (across the Y barrier: the tile is complete from X on).
+  // read VPF steps ahead.
   constexpr int VPF = 2;
   bf16x8_t vr[VPF];
   auto vfrag = [&](const unsigned char* tb, int st) {
@@ -624,39 +623,35 @@ attend_mfma_kernel(AttendArgs a) {
 
   for (int s = -1;; ++s) {
     lds_barrier();  // X(s): P(s) and the rescale factor are published
-    const bool has = s >= 0 && jp < n_mine;  // this step accumulates tile s
-    const unsigned char* tb = lds + ((s + NSLOT) % NSLOT) * ATILE;
-    if (has) {
-      if (tp == 0) {
-        if constexpr (CSA) set_keys(cp, __builtin_amdgcn_readfirstlane(nk[jp & 7]), a.n_split);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < VPF; ++i) vr[i] = vfrag(tb, i);
-      const int par = s & 1;
-      pb[0] = pbuf[((par * 2 + hb) * 2 + 0) * 64 + lane];
-      pb[1] = pbuf[((par * 2 + hb) * 2 + 1) * 64 + lane];
-      const float alpha = alph[par * 64 + head];
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-      }
-      pv_steps(tb, 0);
-    }
-    lds_barrier();  // Y(s)
     if (s < 0) continue;
-    if (!has) break;
+    if (jp >= n_mine) break;  // this step would accumulate tile s
+    const unsigned char* tb = lds + (s % NSLOT) * ATILE;
+    if (tp == 0) {
+      if constexpr (CSA) set_keys(cp, __builtin_amdgcn_readfirstlane(nk[jp & 7]), a.n_split);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) vr[i] = vfrag(tb, i);
+    const int par = s & 1;
+    pb[0] = pbuf[((par * 2 + hb) * 2 + 0) * 64 + lane];
+    pb[1] = pbuf[((par * 2 + hb) * 2 + 1) * 64 + lane];
+    const float alpha = alph[par * 64 + head];
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    }
+    pv_steps(tb, 0);
     pv_steps(tb, NDT);
     if (tp + 1 == cp.n_tiles) {
       if (a.n_split > 1)
         finish_part(cp, qid_of(jp));
       else
-        finish(cp, 1.f / lsum[(s & 1) * 64 + head]);
+        finish(cp, 1.f / lsum[par * 64 + head]);
       tp = 0;
       if (++jp < n_mine) cp = query_geom<CSA>(a, qid_of(jp));
       else break;  // that was the last tile: step n_tiles - 1 is done
@@ -756,7 +751,7 @@ static hipError_t launch_mfma(const AttendArgs& a, hipStream_t st) {
   const int n_q = a.B * a.T;
   const int n_items = n_q * a.n_split;
   const unsigned blocks = static_cast<unsigned>(n_items < n_cu ? n_items : n_cu);
-  hipLaunchKernelGGL((attend_mfma_kernel<CSA, R>), dim3(blocks), dim3(576), kLdsBytes, st, a);
+  hipLaunchKernelGGL((attend_mfma_kernel<CSA, R>), dim3(blocks), dim3(512), kLdsBytes, st, a);
   if (a.n_split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
