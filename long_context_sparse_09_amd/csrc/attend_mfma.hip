@@ -12,26 +12,28 @@
 // Work decomposition
 //   * Persistent workgroups (one per CU) walk their queries as one stream of 32-key tiles:
 //     the window rows of a query, then its selected (CSA) or visible (HCA) pool rows.
-//   * Eight wavefronts in three roles, pipelined by one tile.  Waves w and w + 4 share a
-//     SIMD; the roles are placed so that every SIMD carries the same matrix work per tile:
-//       - gather (waves 4, 5: rows 0..15 and 16..31): move each tile's 32 key rows (1 KB
+//   * Ten wavefronts in three roles, pipelined by one tile.  Wave w runs on SIMD w mod 4;
+//     each SIMD carries one score and one value wave (and SIMDs 0, 1 a gather wave), so the
+//     softmax and epilogue work of one role overlaps the matrix work of the other:
+//       - gather (waves 8, 9: rows 0..15 and 16..31): move each tile's 32 key rows (1 KB
 //         each) from global memory straight into LDS (buffer_load ... lds, one row
 //         descriptor per row), three tiles ahead, into a ring of four tile buffers.  A
 //         vector-memory issue stalls the issuing wave at the CU's fill rate, so the gather
 //         sits in its own waves; for CSA they also copy the next query's index list into
 //         LDS while the current query's tiles stream, so a query switch waits on nothing;
-//       - score (waves 0, 1 = head block hb): heads [32hb, 32hb+32), all 512 channels.
-//         S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 key rows from LDS, B = the
-//         rotated Q in registers, 32 channel steps), then the online softmax of the tile;
-//         publishes P (bf16) and the rescale factor of the running max;
-//       - value (waves 2, 3, 6, 7 = (hb, kh)): O^T[ch kh, heads hb] += V^T . P^T over channels
-//         [256kh, 256kh+256), with V^T read from the same row-major tile through
-//         ds_read_tr16_b64 (K = V is stored once) and P^T taken from LDS in exactly the
-//         B-operand layout the score wave produced it in.
+//       - score (waves 0..3 = hq): heads [16hq, 16hq+16), all 512 channels.  S^T = K . Q^T
+//         on v_mfma_f32_16x16x32_bf16 (A = 16 key rows from LDS, B = the rotated Q in
+//         registers; two 16-key blocks x 16 channel steps), then the online softmax of the
+//         tile; publishes P (bf16, [head][key] rows) and the rescale factor of the running
+//         max;
+//       - value (waves 4..7 = kq): O^T[channels 128kq .. +128, all 64 heads] += V^T . P^T
+//         on v_mfma_f32_32x32x16_bf16, with V^T read from the same row-major tile through
+//         ds_read_tr16_b64 (K = V is stored once); each V^T fragment serves both 32-head
+//         blocks.
 //     In step s the score waves work on tile s+1, the value waves on tile s and the gather
-//     wave fills tile s+3.  Per tile each SIMD runs 32 matrix instructions: a score wave's
-//     32 (with a gather wave beside it) or two value waves' 16 each.  One workgroup
-//     barrier per step: tile s+1 landed, P(s) published, the buffer of tile s-1 free.
+//     waves fill tile s+3.  Per tile each SIMD runs 32 16x16x32 and 16 32x32x16 matrix
+//     instructions (1024 cycles).  One workgroup barrier per step: tile s+1 landed, P(s)
+//     published, the buffer of tile s-1 free.
 //   * Online softmax in the log2 domain; the running max moves only when a logit exceeds it
 //     by 2^8 (lazy rescale).  The state starts from the sink: max = s_h, sum = 1, value 0.
 //   * RoPE angles are formed per lane in double precision (position x frequency, reduced to
@@ -63,8 +65,9 @@ constexpr int ANK = 32;                    // keys per tile
 constexpr int APITCH = AD * 2;             // LDS bytes per key row (swizzled, no pad)
 constexpr int ATILE = ANK * APITCH;        // bytes per tile buffer
 constexpr int NSLOT = 4;                   // tile ring
-constexpr int P_OFF = NSLOT * ATILE;       // P tiles: [parity][hb][16-key half][64] bf16x8
-constexpr int AL_OFF = P_OFF + 2 * 2 * 2 * 64 * 16;  // rescale factors: [parity][64 heads]
+constexpr int PPITCH = ANK * 2 + 16;      // bytes per head row of a P tile (32 keys, padded)
+constexpr int P_OFF = NSLOT * ATILE;       // P tiles: [parity][64 heads][32 keys] bf16
+constexpr int AL_OFF = P_OFF + 2 * AH * PPITCH;      // rescale factors: [parity][64 heads]
 constexpr int LS_OFF = AL_OFF + 2 * 64 * 4;          // softmax sums at a query's end: [parity][64]
 constexpr int KL_OFF = LS_OFF + 2 * 64 * 4;          // gather waves' key lists (CSA) [parity]
 constexpr int kMaxTopk = 1024;                       // key-list capacity on this path
@@ -102,6 +105,15 @@ constexpr int kNT = 2;  // cache policy bits of the buffer instructions: non-tem
 __device__ __forceinline__ float xhalf_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Partner value across the 16-lane rows of each 32-lane half (lane l <-> lane l ^ 16), combined.
+__device__ __forceinline__ float xrow_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float xhalf_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -204,7 +216,7 @@ __device__ __forceinline__ void set_keys(QInfo& d, int n_cmp, int n_split) {
 }
 
 template <bool CSA, int R>  // R = rotary channels, 0 or 64 (compile-time: only those chunks move)
-__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(640, 640), amdgpu_waves_per_eu(3, 3)))
 attend_mfma_kernel(AttendArgs a) {
   static_assert(R == 0 || R == 64, "rotary width on this path");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -228,11 +240,11 @@ attend_mfma_kernel(AttendArgs a) {
   const int n_mine = (n_q - slot + G - 1) / G;
   auto qid_of = [&](int j) { return n_q - 1 - (j * G + slot); };
 
-  if (wave == 4 || wave == 5) {
+  if (wave >= 8) {
     // ------------------------------------------------------------------ gather waves
-    // Wave 4 moves rows 0..15 of every tile, wave 5 rows 16..31; both walk the same cursor.
+    // Wave 8 moves rows 0..15 of every tile, wave 9 rows 16..31; both walk the same cursor.
     __builtin_amdgcn_s_setprio(3);  // its issue slots go first: the other waves wait on its tiles
-    const int gh = wave - 4;
+    const int gh = wave - 8;
     const bf16_t* win0 = static_cast<const bf16_t*>(a.kv_win);
     const bf16_t* pool0 = static_cast<const bf16_t*>(a.pool);
     int* kl = reinterpret_cast<int*>(lds + KL_OFF);  // [query parity][kMaxTopk]
@@ -365,58 +377,60 @@ attend_mfma_kernel(AttendArgs a) {
     return;
   }
 
-  const int half = lane >> 5, l32 = lane & 31;
-  const bool scorer = wave < 2;
-  const int hb = wave & 1;                    // head block of a score or value wave
-  const int kh = scorer ? 0 : (wave >> 2);    // channel half of a value wave
-  const int head = hb * 32 + l32;
-  constexpr int NKS = AD / 16;      // channel steps of QK^T per score wave
-  constexpr int NDT = AD / 2 / 32;  // output channel tiles per value wave
-  bf16x8_t* pbuf = reinterpret_cast<bf16x8_t*>(lds + P_OFF);  // [parity][hb][ss][64]
-  float* alph = reinterpret_cast<float*>(lds + AL_OFF);        // [parity][64 heads]
-  float* lsum = reinterpret_cast<float*>(lds + LS_OFF);        // [parity][64 heads]
+  float* alph = reinterpret_cast<float*>(lds + AL_OFF);  // [parity][64 heads]
+  float* lsum = reinterpret_cast<float*>(lds + LS_OFF);  // [parity][64 heads]
 
-  if (scorer) {
+  if (wave < 4) {
     // ------------------------------------------------------------------ score waves
+    // Wave hq: heads [16hq, 16hq + 16), all channels.  S^T = K . Q^T per tile as two 16-key
+    // blocks kb on v_mfma_f32_16x16x32_bf16: A = 16 key rows x 32 channels (LDS), B = 32
+    // channels x 16 heads (registers).  Lane (h16, g4): head 16hq + h16; it holds keys
+    // 16kb + 4g4 + v of that head and channels 32ks + 8g4 .. + 7 of its Q fragments.
+    const int hq = wave;
+    const int h16 = lane & 15, g4 = lane >> 4;
+    const int head = hq * 16 + h16;
+    constexpr int NKS = AD / 32;  // channel steps of 32
     const float c2 = a.scale * kLog2e;  // logits in the log2 domain
     const float sink2 = a.sink[head] * kLog2e;
-    // Q^T (B operand): head, channels ks*16 + half*8 .. + 7
     bf16x8_t qf[NKS];
-    const unsigned qvoff = static_cast<unsigned>((head * AD + half * 8) * 2);
+    const unsigned qvoff = static_cast<unsigned>((head * AD + 8 * g4) * 2);
     auto load_q = [&](const QInfo& d) {
       const rsrc_t q_rs = make_rs(qbase + (static_cast<size_t>(d.b) * a.T + d.t) * AH * AD, AH * AD * 2);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qvoff + ks * 32, 0, kNT));
+        qf[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(q_rs, qvoff + ks * 64, 0, kNT));
     };
-    // rotary channels AD-R .. AD-1 = the last R/16 channel steps; pair index (channel - (AD-R))/2
+    // rotary channels AD-R .. AD-1 = the last R/32 channel steps; this lane's pair i/2 of
+    // step ks has index (32 ks + 8 g4 + i - (AD - R)) / 2
     auto rotate_q = [&](const QInfo& d) {
       if (R == 0) return;
       const double pos = static_cast<double>(d.p + a.pos_off);
 #pragma unroll
-      for (int ks = NKS - R / 16; ks < NKS; ++ks) {
-        const int pr0 = (ks * 16 - (AD - R)) >> 1;  // pair of this lane: pr0 + 4 half + i/2
+      for (int ks = NKS - R / 32; ks < NKS; ++ks) {
+        const int pr0 = ((ks * 32 - (AD - R)) >> 1) + 4 * g4;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
-          // both candidates at fixed offsets: scalar loads, no vector-memory wait
-          const double f0 = invf[pr0 + i / 2], f1 = invf[pr0 + 4 + i / 2];
           float c, sn;
-          rope_pair(pos, half ? f1 : f0, c, sn);
+          rope_pair(pos, invf[pr0 + i / 2], c, sn);
           const float xv = static_cast<float>(qf[ks][i]), yv = static_cast<float>(qf[ks][i + 1]);
           qf[ks][i] = static_cast<__bf16>(xv * c - yv * sn);
           qf[ks][i + 1] = static_cast<__bf16>(xv * sn + yv * c);
         }
       }
     };
-    // QK^T A operand of step ks: row l32, chunk 2ks + half, at byte qk_base ^ (32 ks) (the
-    // chunk's low 4 bits are XOR-ed with swz(l32))
-    const int qk_base = l32 * APITCH + ((half ^ swz(l32)) << 4);
+    // A operand (kb, ks): key row 16kb + h16, chunk 4ks + g4 at chunk (4ks + g4) ^ swz(h16):
+    // byte kaddr0 + 16 KB kb, XOR 64 ks
+    const int kaddr0 = h16 * APITCH + ((g4 ^ swz(h16)) << 4);
+    // P row of this lane's head.  Within each 16-key block the key index has bits 2 and 3
+    // swapped: a transposing V^T read gives lane (l32, half) keys 4half + 0..3 and
+    // 8 + 4half + 0..3 of the block as its 8 B-operand values, so that these 8 keys sit in
+    // 16 contiguous bytes.  Keys 16kb + 4g4 .. + 3 go to byte 2 (16kb + 4 swap(g4)).
+    unsigned char* prow = lds + P_OFF + head * PPITCH + 8 * (((g4 & 1) << 1) | (g4 >> 1));
 
     int jq = 0, tq = 0;  // cursor: query rank, tile within it
     QInfo cq = query_geom<CSA>(a, qid_of(0));
     load_q(cq);
     float m_run = sink2, l_run = 1.f;
-    f32x16_t sacc;
     for (int s = -1;; ++s) {
       lds_barrier();  // X(s): tile s + 1 has landed
       if (jq >= n_mine) break;  // this step would score tile s + 1
@@ -428,61 +442,61 @@ attend_mfma_kernel(AttendArgs a) {
       }
       const bool last = (tq + 1 == cq.n_tiles);
       const unsigned char* tb = lds + ((s + 1) % NSLOT) * ATILE;
+      f32x4_t sacc[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-      constexpr int PF = 6;  // K fragments in flight
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      constexpr int NI = 2 * NKS;  // matrix instructions per tile: i = 2 ks + kb
+      constexpr int PF = 6;        // K fragments in flight
       bf16x8_t kr[PF];
+      auto kfrag = [&](int i) {
+        return *reinterpret_cast<const bf16x8_t*>(tb + ((kaddr0 + (i & 1) * (16 * APITCH)) ^ (64 * (i >> 1))));
+      };
 #pragma unroll
-      for (int i = 0; i < PF; ++i) kr[i] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * i)));
+      for (int i = 0; i < PF; ++i) kr[i] = kfrag(i);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8_t kf = kr[ks % PF];
-        if (ks + PF < NKS)
-          kr[ks % PF] = *reinterpret_cast<const bf16x8_t*>(tb + (qk_base ^ (32 * (ks + PF))));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+      for (int i = 0; i < NI; ++i) {
+        const bf16x8_t kf = kr[i % PF];
+        if (i + PF < NI) kr[i % PF] = kfrag(i + PF);
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i >> 1], sacc[i & 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (last && jq + 1 < n_mine) load_q(query_geom<CSA>(a, qid_of(jq + 1)));  // next Q streams in
-      // online softmax over the tile's 32 keys (lane: head l32, keys (e/4)*8 + half*4 + e%4)
-      const int kbase = (cq.tb + tq) * ANK + half * 4;
+      // online softmax over the tile's 32 keys: this lane holds keys 16kb + 4g4 + v
+      const int kbase = (cq.tb + tq) * ANK + 4 * g4;
+      float sv[8];
       float tmax = -INFINITY;
-      if ((cq.tb + tq) * ANK + ANK > cq.n_keys) {
+      const bool ragged = (cq.tb + tq) * ANK + ANK > cq.n_keys;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kbase + (e >> 2) * 8 + (e & 3);
-          sacc[e] = key < cq.n_keys ? sacc[e] * c2 : -INFINITY;
-          tmax = fmaxf(tmax, sacc[e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sacc[e] *= c2;
-          tmax = fmaxf(tmax, sacc[e]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int key = kbase + (e >> 2) * 16 + (e & 3);
+        sv[e] = (!ragged || key < cq.n_keys) ? sacc[e >> 2][e & 3] * c2 : -INFINITY;
+        tmax = fmaxf(tmax, sv[e]);
       }
+      tmax = xrow_max(tmax);
       tmax = xhalf_max(tmax);
       const float m_new = (tmax > m_run + kLazy) ? tmax : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float psum = 0.f;
-      bf16x8_t pb0, pb1;  // keys 0..15 and 16..31 of the tile
+      float pe[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[e] - m_new);
-        psum += pv;
-        if (e < 8) pb0[e] = static_cast<__bf16>(pv);
-        else pb1[e - 8] = static_cast<__bf16>(pv);
+      for (int e = 0; e < 8; ++e) {
+        pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
+        psum += pe[e];
       }
-      psum = xhalf_sum(psum);
+      psum = xhalf_sum(xrow_sum(psum));
       l_run = l_run * alpha + psum;
       m_run = m_new;
       const int par = (s + 1) & 1;
-      pbuf[((par * 2 + hb) * 2 + 0) * 64 + lane] = pb0;
-      pbuf[((par * 2 + hb) * 2 + 1) * 64 + lane] = pb1;
-      if (half == 0) {
+      unsigned char* pr = prow + par * (AH * PPITCH);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        *reinterpret_cast<u32x2_t*>(pr + 32 * kb) =
+            u32x2_t{pack_bf16x2(pe[4 * kb], pe[4 * kb + 1]), pack_bf16x2(pe[4 * kb + 2], pe[4 * kb + 3])};
+      if (g4 == 0) {
         alph[par * 64 + head] = alpha;
         if (last) lsum[par * 64 + head] = l_run;
       }
-      if (a.n_split > 1 && last && half == 0) {
+      if (a.n_split > 1 && last && g4 == 0) {
         // split mode: this key range's running max and sum (log2 domain, sink included)
         float* ml = a.part + static_cast<size_t>(n_q) * AH * AD + (static_cast<size_t>(qid_of(jq)) * AH + head) * 2;
         ml[0] = m_run;
@@ -499,32 +513,38 @@ attend_mfma_kernel(AttendArgs a) {
   }
 
   // -------------------------------------------------------------------- value waves
-  // PV transposing reads of dim tile dt, key half ss: rows 16ss + 4*half + i (lo) and
-  // + 8 (hi), i = n16/4; channels kh*256 + dt*32 + dh*16 + 4*(n16%4), i.e. chunk
-  // kh*32 + 4dt + j, j = 2dh + (n16%4)/2.  With swz(row) = 4i + (half | 2hi) the chunk's
-  // bits 2-3 become (dt%4) ^ i and bits 0-1 j ^ (half | 2hi): the byte offset is
-  // (tr_lo or tr_hi) ^ (64 (dt%4)), plus 256 (dt/4) and 16 KB ss.
+  // Wave 4 + kq: output channels [128kq, 128kq + 128) of all 64 heads.  O^T[32 ch x 32 heads]
+  // blocks (cb, hb) += V^T[32 ch x 16 keys] . P^T[16 keys x 32 heads] per 16-key half ks;
+  // each V^T fragment serves both head blocks.  Lane (l32, half): head 32hb + l32, channels
+  // 8q + 4half + j of each 32-channel block (q = 0..3).
+  const int kq = wave - 4;
+  const int half = lane >> 5, l32 = lane & 31;
+  constexpr int NCB = 4;  // 32-channel blocks per wave
+  // V^T transposing reads of channel block cb, key half ks: rows 16ks + 4half + i (lo) and
+  // + 8 (hi), i = n16/4; channels 128kq + 32cb + 16dh + 4(n16%4), i.e. chunk 16kq + 4cb + j,
+  // j = 2dh + (n16%4)/2.  With swz(row) = 4i + (half | 2hi) the chunk's bits 2-3 become
+  // cb ^ i and bits 0-1 j ^ (half | 2hi): the byte offset is (tr_lo or tr_hi) ^ (64 cb),
+  // plus 16 KB ks.
   int tr_lo, tr_hi;
   {
     const int n16 = lane & 15, dh = (lane >> 4) & 1;
     const int i = n16 >> 2, j = 2 * dh + ((n16 & 3) >> 1);
-    const int common = kh * (AD / 2) * 2 + 64 * i + (n16 & 1) * 8;
+    const int common = 256 * kq + 64 * i + (n16 & 1) * 8;
     tr_lo = (4 * half + i) * APITCH + common + 16 * (j ^ half);
     tr_hi = (4 * half + i + 8) * APITCH + common + 16 * (j ^ (half | 2));
   }
-  f32x16_t o[NDT];
+  f32x16_t o[NCB][2];
   int jp = 0, tp = 0;  // cursor: query rank, tile within it
   QInfo cp = query_geom<CSA>(a, qid_of(0));
-  bf16x8_t pb[2];
-  // PV runs as one stream of 16 steps st = 16-key half * NDT + dt, whose V fragments are
-  // read VPF steps ahead.
+  // PV runs as one stream of 8 steps st = ks * NCB + cb (two matrix instructions each),
+  // whose V fragments are read VPF steps ahead.
   constexpr int VPF = 2;
   bf16x8_t vr[VPF];
   auto vfrag = [&](const unsigned char* tb, int st) {
-    const unsigned char* vb = tb + 16 * (st / NDT) * APITCH + 256 * ((st % NDT) >> 2);
-    // the XOR is formed at each read (volatile asm is not hoisted): keeping eight
-    // pre-XOR-ed offsets live would push the accumulators out of registers
-    const int x = 64 * (st & 3);
+    const unsigned char* vb = tb + 16 * (st / NCB) * APITCH;
+    // the XOR is formed at each read (volatile asm is not hoisted): keeping pre-XOR-ed
+    // offsets live would push the accumulators out of registers
+    const int x = 64 * (st % NCB);
     int olo, ohi;
     asm volatile("v_xor_b32 %0, %1, %2" : "=v"(olo) : "v"(tr_lo), "s"(x));
     asm volatile("v_xor_b32 %0, %1, %2" : "=v"(ohi) : "v"(tr_hi), "s"(x));
@@ -532,37 +552,75 @@ attend_mfma_kernel(AttendArgs a) {
     const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + ohi));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto pv_steps = [&](const unsigned char* tb, int st0) {  // steps st0 .. st0 + NDT - 1
-#pragma unroll
-    for (int i = 0; i < NDT; ++i) {
-      const int st = st0 + i;
-      const bf16x8_t vf = vr[st % VPF];
-      if (st + VPF < 2 * NDT) vr[st % VPF] = vfrag(tb, st + VPF);
-      o[st % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[st / NDT], o[st % NDT], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
   // epilogue of one query: normalise, counter-rotate (eq. 26), store.  A 32-lane swap pairs
   // the two 4-channel halves so that each lane writes 16 contiguous bytes.
-  const unsigned ovoff = static_cast<unsigned>((head * AD + kh * (AD / 2) + half * 8) * 2);
-  auto finish = [&](const QInfo& d, float inv) {
+  auto finish = [&](const QInfo& d, const float (&inv)[2]) {
     const rsrc_t o_rs = make_rs(static_cast<bf16_t*>(a.out) + (static_cast<size_t>(d.b) * a.T + d.t) * AH * AD,
                                 AH * AD * 2);
     const double pos = -static_cast<double>(d.p + a.pos_off);  // the same angle, negated
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    for (int hb = 0; hb < 2; ++hb) {
+      const unsigned ovoff = static_cast<unsigned>(((32 * hb + l32) * AD + 128 * kq + half * 8) * 2);
 #pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        unsigned w[2][2];
+      for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-          const int gq = 2 * gp + g2;
+        for (int gp = 0; gp < 2; ++gp) {
+          unsigned w[2][2];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int gq = 2 * gp + g2;
+            float v[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) v[jj] = o[cb][hb][gq * 4 + jj] * inv[hb];
+            const int cl0 = 128 * kq + cb * 32 + gq * 8;  // channel: cl0 + 4 half + jj
+            if (R > 0 && cl0 >= AD - R) {
+              const int pr0 = (cl0 - (AD - R)) >> 1;  // pair: pr0 + 2 half + i2/2
+#pragma unroll
+              for (int i2 = 0; i2 < 4; i2 += 2) {
+                const double f0 = invf[pr0 + i2 / 2], f1 = invf[pr0 + 2 + i2 / 2];
+                float c, sn;
+                rope_pair(pos, half ? f1 : f0, c, sn);
+                const float xv = v[i2], yv = v[i2 + 1];
+                v[i2] = xv * c - yv * sn;
+                v[i2 + 1] = xv * sn + yv * c;
+              }
+            }
+            w[g2][0] = pack_bf16x2(v[0], v[1]);
+            w[g2][1] = pack_bf16x2(v[2], v[3]);
+          }
+          // lanes < 32 collect group 2gp (channels +0..7), lanes >= 32 group 2gp+1
+          const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
+          u32x4_t val;
+          val[0] = s0[0];
+          val[1] = s1[0];
+          val[2] = s0[1];
+          val[3] = s1[1];
+          // lanes >= 32 write group 2gp + 1: their half * 8 channels are part of ovoff
+          __builtin_amdgcn_raw_buffer_store_b128(val, o_rs, ovoff + (cb * 32 + 2 * gp * 8) * 2, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);  // one group at a time: keeps the epilogue's registers few
+        }
+      }
+    }
+  };
+
+  // split mode: the unnormalised output of this key range, counter-rotated (the rotation is
+  // linear, so it commutes with the merge), as fp32 rows of the workspace
+  auto finish_part = [&](const QInfo& d, int item) {
+    const double pos = -static_cast<double>(d.p + a.pos_off);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float* po = a.part + (static_cast<size_t>(item) * AH + 32 * hb + l32) * AD + half * 4;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
           float v[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) v[jj] = o[dt][gq * 4 + jj] * inv;
-          const int cl0 = dt * 32 + gq * 8;  // channel within this wave's half: cl0 + 4 half
-          if (R > 0 && kh == 1 && cl0 >= AD / 2 - R) {
-            const int pr0 = (cl0 - (AD / 2 - R)) >> 1;  // pair: pr0 + 2 half + i2/2
+          for (int jj = 0; jj < 4; ++jj) v[jj] = o[cb][hb][gq * 4 + jj];
+          const int cl0 = 128 * kq + cb * 32 + gq * 8;
+          if (R > 0 && cl0 >= AD - R) {
+            const int pr0 = (cl0 - (AD - R)) >> 1;
 #pragma unroll
             for (int i2 = 0; i2 < 4; i2 += 2) {
               const double f0 = invf[pr0 + i2 / 2], f1 = invf[pr0 + 2 + i2 / 2];
@@ -573,50 +631,8 @@ attend_mfma_kernel(AttendArgs a) {
               v[i2 + 1] = xv * sn + yv * c;
             }
           }
-          w[g2][0] = pack_bf16x2(v[0], v[1]);
-          w[g2][1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<f32x4_t*>(po + cl0) = f32x4_t{v[0], v[1], v[2], v[3]};
         }
-        // lanes < 32 collect group 2gp (channels +0..7), lanes >= 32 group 2gp+1
-        const auto s0 = __builtin_amdgcn_permlane32_swap(w[0][0], w[1][0], false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(w[0][1], w[1][1], false, false);
-        u32x4_t val;
-        val[0] = s0[0];
-        val[1] = s1[0];
-        val[2] = s0[1];
-        val[3] = s1[1];
-        // lanes >= 32 write group 2gp + 1: their half * 8 channels are part of ovoff
-        __builtin_amdgcn_raw_buffer_store_b128(val, o_rs, ovoff + (dt * 32 + 2 * gp * 8) * 2, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);  // one group at a time: keeps the epilogue's registers few
-      }
-    }
-  };
-
-  // split mode: the unnormalised output of this key range, counter-rotated (the rotation is
-  // linear, so it commutes with the merge), as fp32 rows of the workspace
-  auto finish_part = [&](const QInfo& d, int item) {
-    float* po = a.part + (static_cast<size_t>(item) * AH + head) * AD + kh * (AD / 2) + half * 4;
-    const double pos = -static_cast<double>(d.p + a.pos_off);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float v[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) v[jj] = o[dt][gq * 4 + jj];
-        const int cl0 = dt * 32 + gq * 8;
-        if (R > 0 && kh == 1 && cl0 >= AD / 2 - R) {
-          const int pr0 = (cl0 - (AD / 2 - R)) >> 1;
-#pragma unroll
-          for (int i2 = 0; i2 < 4; i2 += 2) {
-            const double f0 = invf[pr0 + i2 / 2], f1 = invf[pr0 + 2 + i2 / 2];
-            float c, sn;
-            rope_pair(pos, half ? f1 : f0, c, sn);
-            const float xv = v[i2], yv = v[i2 + 1];
-            v[i2] = xv * c - yv * sn;
-            v[i2 + 1] = xv * sn + yv * c;
-          }
-        }
-        *reinterpret_cast<f32x4_t*>(po + cl0) = f32x4_t{v[0], v[1], v[2], v[3]};
       }
     }
   };
@@ -629,29 +645,53 @@ attend_mfma_kernel(AttendArgs a) {
     if (tp == 0) {
       if constexpr (CSA) set_keys(cp, __builtin_amdgcn_readfirstlane(nk[jp & 7]), a.n_split);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[cb][hb][e] = 0.f;
     }
 #pragma unroll
     for (int i = 0; i < VPF; ++i) vr[i] = vfrag(tb, i);
     const int par = s & 1;
-    pb[0] = pbuf[((par * 2 + hb) * 2 + 0) * 64 + lane];
-    pb[1] = pbuf[((par * 2 + hb) * 2 + 1) * 64 + lane];
-    const float alpha = alph[par * 64 + head];
-    if (__ballot(alpha != 1.f)) {
+    // P^T fragments (ks, hb): head 32hb + l32, keys 16ks + 4half + 0..3 and + 8 (stored
+    // contiguously at 16ks + 8half, see the score waves)
+    const unsigned char* pt = lds + P_OFF + par * (AH * PPITCH) + l32 * PPITCH + 16 * half;
+    bf16x8_t pb[2];  // the current key half's fragments, one per head block
+    auto pfrag = [&](int ks) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int hb = 0; hb < 2; ++hb)
+        pb[hb] = *reinterpret_cast<const bf16x8_t*>(pt + hb * (32 * PPITCH) + 32 * ks);
+    };
+    pfrag(0);
+    float alpha[2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    for (int hb = 0; hb < 2; ++hb) alpha[hb] = alph[par * 64 + 32 * hb + l32];
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[cb][hb][e] *= alpha[hb];
     }
-    pv_steps(tb, 0);
-    pv_steps(tb, NDT);
+#pragma unroll
+    for (int st = 0; st < 2 * NCB; ++st) {
+      if (st == NCB) pfrag(1);  // the first half's fragments are done
+      const bf16x8_t vf = vr[st % VPF];
+      if (st + VPF < 2 * NCB) vr[st % VPF] = vfrag(tb, st + VPF);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        o[st % NCB][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[hb], o[st % NCB][hb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (tp + 1 == cp.n_tiles) {
-      if (a.n_split > 1)
+      if (a.n_split > 1) {
         finish_part(cp, qid_of(jp));
-      else
-        finish(cp, 1.f / lsum[par * 64 + head]);
+      } else {
+        const float inv[2] = {1.f / lsum[par * 64 + l32], 1.f / lsum[par * 64 + 32 + l32]};
+        finish(cp, inv);
+      }
       tp = 0;
       if (++jp < n_mine) cp = query_geom<CSA>(a, qid_of(jp));
       else break;  // that was the last tile: step n_tiles - 1 is done
@@ -751,7 +791,7 @@ static hipError_t launch_mfma(const AttendArgs& a, hipStream_t st) {
   const int n_q = a.B * a.T;
   const int n_items = n_q * a.n_split;
   const unsigned blocks = static_cast<unsigned>(n_items < n_cu ? n_items : n_cu);
-  hipLaunchKernelGGL((attend_mfma_kernel<CSA, R>), dim3(blocks), dim3(512), kLdsBytes, st, a);
+  hipLaunchKernelGGL((attend_mfma_kernel<CSA, R>), dim3(blocks), dim3(640), kLdsBytes, st, a);
   if (a.n_split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
