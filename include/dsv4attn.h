@@ -205,6 +205,34 @@ int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
                double rope_theta, long long rope_pos_offset, float scale, void* workspace,
                size_t workspace_bytes, int dtype, void* stream);
 
+/*
+ * attention_mask_dump - render one layer's attention visibility for auditing ("Attention mask
+ * layout": the sliding / CSA / HCA mask diagrams of the 16-token example and the audit script
+ * described with them, which draws the masks as SVG, prints a terminal grid and dumps the
+ * indexer's per-query selections so that warm-up sentinels and picks can be checked).
+ * Host code only: no device memory is touched.
+ *
+ * Rows are queries t = 0 .. S-1 at sequence indices q_pos0 + t.  Columns are the key
+ * positions 0 .. q_pos0 + S - 1, then one column per compressed entry C_0 .. C_{n_entries-1}
+ * (the entry-visibility view, not gather slots).  Key j is visible to the query at p when
+ * max(0, p - window + 1) <= j <= p.  Entry w can be visible once w < min((p + 1) / m,
+ * n_entries); HCA (kind 2) marks every such entry, CSA (kind 1) marks the entries its index
+ * list selects, shows the other candidates as visible-but-not-selected, and flags a listed
+ * entry that is not visible.  A sliding layer (kind 0) has no entry columns.
+ *
+ *   kind : 0 sliding, 1 CSA, 2 HCA.  m : compress rate (kind 1, 2).
+ *   topk_idx : host int32 [S][k] (kind 1; the lists csa_index_topk wrote, -1 = empty slot).
+ *   format : 0 plain text grid, 1 the same with ANSI colours, 2 SVG, 3 per-query index lists
+ *            with the count of empty slots.
+ *   buf, buf_bytes : caller-owned output buffer; *needed receives the bytes the output takes
+ *            (including the terminating NUL).  With buf NULL or too small nothing is written
+ *            and DSV4_ERR_WORKSPACE is returned, so a first call with buf = NULL sizes it.
+ *   At most 2^24 cells (S x columns): DSV4_ERR_UNSUPPORTED beyond.
+ */
+int attention_mask_dump(int kind, int S, int window, int m, const int* topk_idx, int k,
+                        int n_entries, long long q_pos0, int format, char* buf, size_t buf_bytes,
+                        size_t* needed);
+
 #ifdef __cplusplus
 }
 #endif

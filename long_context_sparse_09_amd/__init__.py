@@ -11,8 +11,9 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["csa_compress", "csa_index_topk", "csa_index_topk_workspace_size", "swa_concat",
-           "csa_attend", "hca_attend", "abi_version", "DSV4Error", "lib"]
+__all__ = ["csa_compress", "compressor_cache_update", "csa_index_topk",
+           "csa_index_topk_workspace_size", "swa_concat", "csa_attend", "hca_attend",
+           "attend_workspace_size", "attention_mask_dump", "abi_version", "DSV4Error", "lib"]
 
 DSV4_FP32, DSV4_BF16 = 0, 1
 
@@ -160,3 +161,31 @@ def hca_attend(q, kv_win, kv_pos0, pool, n_pool, m_hca: int, sink, q_pos0, out, 
         m_hca, _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D, window, rope_dim,
         float(rope_theta), int(rope_pos_offset), float(scale), wp, wb, _dtype(q),
         _stream(stream)))
+
+
+_MASK_KINDS = {"sliding": 0, "csa": 1, "hca": 2}
+_MASK_FORMATS = {"text": 0, "ansi": 1, "svg": 2, "lists": 3}
+
+
+def attention_mask_dump(kind: str, S: int, window: int, m: int = 1, topk_idx=None,
+                        n_entries: int = 0, q_pos0: int = 0, fmt: str = "text") -> str:
+    """Visibility grid / SVG / index-list dump of one layer (host only).  topk_idx: [S, k]
+    int32 lists (numpy array or tensor; copied to host memory) for kind "csa"."""
+    import ctypes
+
+    import numpy as np
+
+    ptr, k, keep = None, 0, None
+    if topk_idx is not None:
+        if hasattr(topk_idx, "detach"):
+            topk_idx = topk_idx.detach().cpu().numpy()
+        keep = np.ascontiguousarray(np.asarray(topk_idx, dtype=np.int32).reshape(S, -1))
+        ptr, k = keep.ctypes.data, keep.shape[1]
+    args = (_MASK_KINDS[kind], S, window, m, ptr, k, n_entries, q_pos0, _MASK_FORMATS[fmt])
+    need = ctypes.c_size_t(0)
+    st = lib().attention_mask_dump(*args, None, 0, ctypes.byref(need))
+    if st != 4:  # anything but "buffer too small" is a real error
+        _check("attention_mask_dump", st)
+    buf = ctypes.create_string_buffer(need.value)
+    _check("attention_mask_dump", lib().attention_mask_dump(*args, buf, need.value, ctypes.byref(need)))
+    return buf.value.decode()

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "../../include/dsv4attn.h"
 #include "common.h"
@@ -116,6 +117,28 @@ int compressor_cache_update(const void* x_new, const void* gate_new, void* x_rin
                                             rope_theta, rope_pos_offset, emit, dtype,
                                             static_cast<hipStream_t>(stream)),
                   "compressor_cache_update");
+}
+
+int attention_mask_dump(int kind, int S, int window, int m, const int* topk_idx, int k,
+                        int n_entries, long long q_pos0, int format, char* buf, size_t buf_bytes,
+                        size_t* needed) {
+  REQUIRE(kind >= 0 && kind <= 2, "kind %d: 0 sliding, 1 CSA, 2 HCA", kind);
+  REQUIRE(format >= 0 && format <= 3, "format %d: 0 text, 1 ANSI, 2 SVG, 3 index lists", format);
+  REQUIRE(S >= 0 && q_pos0 >= 0 && window >= 1, "S, q_pos0 must be >= 0 and window >= 1");
+  REQUIRE(kind == 0 || (m >= 1 && n_entries >= 0), "m must be >= 1 and n_entries >= 0");
+  REQUIRE(kind != 1 || (k >= 1 && (S == 0 || topk_idx)), "CSA needs the index lists (k >= 1)");
+  REQUIRE(needed != nullptr, "needed must not be NULL");
+  const long long width = q_pos0 + S + (kind == 0 ? 0 : n_entries);
+  if (static_cast<long long>(S) * width > (1LL << 24))
+    return fail(DSV4_ERR_UNSUPPORTED, "%lld cells: at most 2^24", static_cast<long long>(S) * width);
+  dsv4::MaskDumpArgs a{kind, S, window, m, kind == 1 ? k : 0, kind == 0 ? 0 : n_entries, format, q_pos0,
+                       topk_idx};
+  const std::string out = dsv4::render_mask(a);
+  *needed = out.size() + 1;
+  if (buf == nullptr || buf_bytes < out.size() + 1)
+    return fail(DSV4_ERR_WORKSPACE, "output needs %zu bytes", out.size() + 1);
+  memcpy(buf, out.c_str(), out.size() + 1);
+  return ok();
 }
 
 size_t csa_index_topk_workspace_size(int B, int T, int N_cap, int k) {

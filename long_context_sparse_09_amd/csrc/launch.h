@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <string>
+
 namespace dsv4 {
 
 hipError_t launch_compress(const void* x, const void* gate, const float* bias, void* pool, int B,
@@ -69,5 +71,14 @@ bool attend_fast(int H, int D, int r, int dtype);
 bool attend_uses_fast(const AttendArgs& a);
 // Keys one query may see at most (sizes the generic attention kernel's LDS).
 int attend_generic_max_keys();
+
+// Visibility rendering of one layer (host only).  kind 0 sliding, 1 CSA, 2 HCA; format 0 text,
+// 1 ANSI text, 2 SVG, 3 per-query index lists.  topk_idx: host [S][k] (CSA).
+struct MaskDumpArgs {
+  int kind, S, window, m, k, n_entries, format;
+  long long q_pos0;
+  const int* topk_idx;
+};
+std::string render_mask(const MaskDumpArgs& a);
 
 }  // namespace dsv4
