@@ -30,6 +30,10 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
   visibility               pinned: the page's 16-token worked example
   attend_query             pinned: torch SDPA (fp64) with explicit K=V and sink column,
                            sink closed forms, eq. 26 shift invariance
+  grouped_out_proj         pinned: brute-force loops on tiny shapes, group locality (a group's
+                           heads reach only its rank slice), identity weights.  The grouping
+                           of consecutive heads and the linear-layer weight layout are
+                           readings (R22); the page prints no values for them.
 """
 from __future__ import annotations
 
@@ -402,3 +406,39 @@ def hca_layer(inp: dict, cfg, rows=None, round_intermediates: bool = False, pos_
     out = hca_attend(inp["q"], kv_win, zeros, pool, npool, cfg.m_hca, inp["sink"], zeros, cfg.W,
                      cfg.r, cfg.base, pos_offset, rows=rows)
     return out, dict(pool=pool, kv_win=kv_win)
+
+
+# ----------------------------------------------------------------------------
+# grouped low-rank output projection (the step right after the attention core)
+# ----------------------------------------------------------------------------
+
+
+def grouped_out_proj(attn, w_a, w_b, groups: int, round_intermediate: bool = False):
+    """Grouped low-rank output projection.
+
+    "Hybrid attention (§2.3)", grouped output projection item (o_groups head groups ->
+    o_lora_rank per group -> hidden_size, a grouped linear o_a_proj then o_b_proj) and
+    "DeepseekV4Config" (o_groups, o_lora_rank, hidden_size).  Reading R22: the H heads split
+    into `groups` runs of H/groups consecutive heads; group g's head outputs, concatenated
+    (H/groups * D values), are multiplied by its own matrix w_a[g] of shape
+    [rank, H/groups * D] (a linear layer's [out, in] layout); the groups' rank vectors,
+    concatenated in group order, are multiplied by w_b [hidden, groups * rank].  No bias
+    (attention_bias is False) and nothing between the two products.
+    ``round_intermediate`` models bf16 storage of the [T, groups * rank] intermediate.
+
+    attn [T, H, D] or [T, H * D]; returns (out [T, hidden], intermediate [T, groups * rank]).
+    """
+    a = np.asarray(attn, dtype=np.float64)
+    T = a.shape[0]
+    a = a.reshape(T, -1)
+    w_a = np.asarray(w_a, dtype=np.float64)
+    w_b = np.asarray(w_b, dtype=np.float64)
+    assert w_a.shape[0] == groups and a.shape[1] == groups * w_a.shape[2], (a.shape, w_a.shape)
+    rank = w_a.shape[1]
+    kg = w_a.shape[2]
+    mid = np.empty((T, groups * rank))
+    for g in range(groups):
+        mid[:, g * rank:(g + 1) * rank] = a[:, g * kg:(g + 1) * kg] @ w_a[g].T
+    if round_intermediate:
+        mid = round_bf16(mid)
+    return mid @ w_b.T, mid

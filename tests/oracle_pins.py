@@ -417,4 +417,71 @@ def pin_round_bf16(O):
     assert got[5] == 0.0 and got[6] == 65536.0
 
 
+
+# ----------------------------------------------------------------------------
+# grouped output projection
+# ----------------------------------------------------------------------------
+
+
+def _oproj_case(seed, T=3, H=4, D=3, groups=2, rank=5, hidden=6):
+    r = RNG(seed)
+    attn = r.standard_normal((T, H, D))
+    w_a = r.standard_normal((groups, rank, H // groups * D))
+    w_b = r.standard_normal((hidden, groups * rank))
+    return attn, w_a, w_b, groups
+
+
+def pin_oproj_bruteforce(O):
+    """Explicit loops over every output element on a tiny non-square case."""
+    attn, w_a, w_b, G = _oproj_case(11)
+    T, H, D = attn.shape
+    rank, hidden, hpg = w_a.shape[1], w_b.shape[0], H // G
+    out, mid = O.grouped_out_proj(attn, w_a, w_b, G)
+    want_mid = np.zeros((T, G * rank))
+    for t in range(T):
+        for g in range(G):
+            for j in range(rank):
+                acc = 0.0
+                for hh in range(hpg):
+                    for d in range(D):
+                        acc += attn[t, g * hpg + hh, d] * w_a[g, j, hh * D + d]
+                want_mid[t, g * rank + j] = acc
+    want = np.zeros((T, hidden))
+    for t in range(T):
+        for o in range(hidden):
+            want[t, o] = sum(want_mid[t, i] * w_b[o, i] for i in range(G * rank))
+    _close(mid, want_mid, 1e-12, "intermediate")
+    _close(out, want, 1e-12, "output")
+
+
+def pin_oproj_group_locality(O):
+    """Changing the heads of one group changes only that group's rank slice; a one-hot head
+    lands in the slice of the group of consecutive heads that holds it."""
+    attn, w_a, w_b, G = _oproj_case(12, H=6, groups=3)
+    _, mid0 = O.grouped_out_proj(attn, w_a, w_b, G)
+    rank, hpg = w_a.shape[1], attn.shape[1] // G
+    for g in range(G):
+        a2 = attn.copy()
+        a2[:, g * hpg:(g + 1) * hpg] += 1.0
+        _, mid1 = O.grouped_out_proj(a2, w_a, w_b, G)
+        changed = np.abs(mid1 - mid0).max(axis=0) > 0
+        assert changed[g * rank:(g + 1) * rank].all()
+        assert not np.delete(changed, np.s_[g * rank:(g + 1) * rank]).any(), g
+    one = np.zeros_like(attn)
+    one[0, 1, 0] = 1.0  # head 1 belongs to group 0 (heads 0, 1)
+    _, mid = O.grouped_out_proj(one, w_a, w_b, G)
+    _close(mid[0, :rank], w_a[0, :, attn.shape[2]], 1e-15, "one-hot head 1")
+    assert not mid[0, rank:].any()
+
+
+def pin_oproj_identity(O):
+    """One group, identity weights: the output is the attention output itself."""
+    r = RNG(13)
+    attn = r.standard_normal((4, 2, 3))
+    K = 6
+    out, mid = O.grouped_out_proj(attn, np.eye(K)[None], np.eye(K), 1)
+    _close(out, attn.reshape(4, K), 0.0, "identity")
+    _close(mid, attn.reshape(4, K), 0.0, "identity intermediate")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -51,6 +51,12 @@ MUTATIONS = {
                                    "s = np.asarray(scores, dtype=np.float64)"),
                                   ("key=lambda w: (-s[w], w)",
                                    "key=lambda w: (-s[w], 0 if np.signbit(s[w]) else -1, w)")],
+    "oproj_heads_interleaved": [("mid[:, g * rank:(g + 1) * rank] = a[:, g * kg:(g + 1) * kg] @ w_a[g].T",
+                                 "mid[:, g * rank:(g + 1) * rank] = "
+                                 "np.asarray(attn, dtype=np.float64)[:, g::groups].reshape(T, -1) @ w_a[g].T")],
+    "oproj_group_order_reversed": [("mid[:, g * rank:(g + 1) * rank] = a[:, g * kg:(g + 1) * kg] @ w_a[g].T",
+                                    "mid[:, g * rank:(g + 1) * rank] = a[:, g * kg:(g + 1) * kg] @ w_a[groups - 1 - g].T")],
+    "oproj_second_product_dropped": [("return mid @ w_b.T, mid", "return mid[:, :w_b.shape[0]], mid")],
 }
 
 
