@@ -382,6 +382,40 @@ def cpu_baseline(n_sample=640):
 
 # ----------------------------------------------------------------------------- main
 
+def run_oproj(torch, steps, warmup):
+    """The grouped low-rank output projection after the S=8192 CSA layer: 8192 tokens of
+    64 heads x 512 -> 8 groups x rank 1024 -> hidden 4096 (DeepseekV4Config defaults).  Inputs
+    are generated on the device (N(0,1) attention output, fan-in-scaled N(0,1) weights, bf16)."""
+    import workloads as W
+    from long_context_sparse_09_amd import grouped_out_proj
+
+    w = W.workload(2)
+    T, G, rk, hid = w.S, w.o_groups, w.o_rank, w.hidden
+    kg = w.H // G * w.D
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed * 1000 + 77)
+    attn = torch.randn((T, w.H, w.D), generator=g, device="cuda").to(torch.bfloat16)
+    w_a = (torch.randn((G, rk, kg), generator=g, device="cuda") / kg ** 0.5).to(torch.bfloat16)
+    w_b = (torch.randn((hid, G * rk), generator=g, device="cuda") / (G * rk) ** 0.5).to(torch.bfloat16)
+    mid = torch.empty((T, G * rk), device="cuda", dtype=torch.bfloat16)
+    out = torch.empty((T, hid), device="cuda", dtype=torch.bfloat16)
+    for _ in range(warmup):
+        grouped_out_proj(attn, w_a, w_b, mid, out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        grouped_out_proj(attn, w_a, w_b, mid, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * T * (G * rk * kg + hid * G * rk)
+    return {"workload": "grouped_out_proj T=8192: 64x512 -> 8x1024 -> 4096 (bf16)", "ms": ms,
+            "alg_flops": flops, "TFLOP/s": flops / ms / 1e9, "bound": "mfma",
+            "frac": flops / ms / 1e9 / (PEAK_BF16 / 1e12), "tokens_per_s": T / ms * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -389,7 +423,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA / decode workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["csa_prefill", "hca_prefill", "csa_decode", "stack"], default=None,
+    ap.add_argument("--only", choices=["csa_prefill", "hca_prefill", "csa_decode", "stack", "oproj"], default=None,
                     help="run one workload alone (for profiling); prints its figures only")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="launch one device copy of this size first (counter calibration)")
@@ -410,9 +444,9 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written")
         del src, dst
-    if args.only in ("hca_prefill", "csa_decode", "stack"):
+    if args.only in ("hca_prefill", "csa_decode", "stack", "oproj"):
         fn = {"hca_prefill": run_hca_prefill, "csa_decode": run_decode,
-              "stack": run_stack}[args.only]
+              "stack": run_stack, "oproj": run_oproj}[args.only]
         print(json.dumps({"only": args.only, **fn(torch, args.steps, args.warmup)}), flush=True)
         return
     w, wall, kern = run_csa_prefill(torch, args.steps, args.warmup)
@@ -427,6 +461,8 @@ def main():
         extra["csa_decode"] = run_decode(torch, args.steps, args.warmup)
         torch.cuda.empty_cache()
         extra["stack8_prefill"] = run_stack(torch, max(2, args.steps // 5), 1)
+        torch.cuda.empty_cache()
+        extra["grouped_out_proj"] = run_oproj(torch, args.steps, args.warmup)
         torch.cuda.empty_cache()
     att = kern["csa_attend"]
     src = kernel_hash("attend_mfma.hip", "common.h")

@@ -206,6 +206,35 @@ int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
                size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * grouped_out_proj - grouped low-rank output projection ("Hybrid attention (§2.3)", grouped
+ * output projection item; "DeepseekV4Config": o_groups, o_lora_rank, hidden_size).  Reading:
+ * head group g is the run of H/groups consecutive heads; its concatenated outputs
+ * (H/groups * D values) times its own [rank, H/groups * D] matrix give the group's rank
+ * vector (o_a_proj, a grouped linear); the groups' vectors, concatenated in group order,
+ * times the [hidden, groups * rank] matrix give the output (o_b_proj).  No bias.
+ *
+ *   attn : [T, H, D] dtype (the attention output).  w_a : [groups, rank, H/groups * D].
+ *   w_b  : [hidden, groups * rank].  Weights use a linear layer's [out, in] layout.
+ *   mid  : caller-owned [T, groups * rank] dtype buffer for the intermediate (written).
+ *   out  : [T, hidden] dtype.  Accumulation is fp32; mid is stored in dtype.
+ *   groups must divide H.  Every [T, .] operand below 2 GiB (DSV4_ERR_UNSUPPORTED beyond).
+ *   bf16 with rank and hidden multiples of 256 and H/groups * D, groups * rank multiples of 64
+ *   runs on the MFMA path; other shapes run a plain kernel (same results up to rounding order).
+ */
+int grouped_out_proj(const void* attn, const void* w_a, const void* w_b, void* mid, void* out, int T,
+                     int H, int D, int groups, int rank, int hidden, int dtype, void* stream);
+
+/*
+ * linear_bt - y = x . w^T, the dense product behind the projections around the attention core
+ * (the factors of the grouped output projection above; the upstream projections that feed the
+ * indexer and the attention are products of the same form).
+ *
+ *   x : [M, K] dtype.  w : [N, K] dtype (a linear layer's [out, in] weight).  y : [M, N] dtype.
+ *   fp32 accumulation.  bf16 with N % 256 == 0 and K % 64 == 0 runs on the MFMA path.
+ */
+int linear_bt(const void* x, const void* w, void* y, int M, int N, int K, int dtype, void* stream);
+
+/*
  * attention_mask_dump - render one layer's attention visibility for auditing ("Attention mask
  * layout": the sliding / CSA / HCA mask diagrams of the 16-token example and the audit script
  * described with them, which draws the masks as SVG, prints a terminal grid and dumps the

@@ -13,7 +13,8 @@ from . import _lib
 
 __all__ = ["csa_compress", "compressor_cache_update", "csa_index_topk",
            "csa_index_topk_workspace_size", "swa_concat", "csa_attend", "hca_attend",
-           "attend_workspace_size", "attention_mask_dump", "abi_version", "DSV4Error", "lib"]
+           "attend_workspace_size", "grouped_out_proj", "linear_bt", "attention_mask_dump",
+           "abi_version", "DSV4Error", "lib"]
 
 DSV4_FP32, DSV4_BF16 = 0, 1
 
@@ -161,6 +162,30 @@ def hca_attend(q, kv_win, kv_pos0, pool, n_pool, m_hca: int, sink, q_pos0, out, 
         m_hca, _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D, window, rope_dim,
         float(rope_theta), int(rope_pos_offset), float(scale), wp, wb, _dtype(q),
         _stream(stream)))
+
+
+def grouped_out_proj(attn, w_a, w_b, mid, out, stream=None) -> None:
+    """attn [T,H,D]; w_a [groups,rank,H/groups*D]; w_b [hidden,groups*rank]; mid [T,groups*rank]
+    (written); out [T,hidden]."""
+    T, H, D = attn.shape
+    groups, rank, kg = w_a.shape
+    hidden = w_b.shape[0]
+    if kg * groups != H * D or tuple(w_b.shape) != (hidden, groups * rank):
+        raise ValueError(f"w_a {tuple(w_a.shape)} / w_b {tuple(w_b.shape)} do not fit attn {tuple(attn.shape)}")
+    if tuple(mid.shape) != (T, groups * rank) or tuple(out.shape) != (T, hidden):
+        raise ValueError("mid must be [T, groups*rank] and out [T, hidden]")
+    _check("grouped_out_proj", lib().grouped_out_proj(
+        _ptr(attn), _ptr(w_a), _ptr(w_b), _ptr(mid), _ptr(out), T, H, D, groups, rank, hidden,
+        _dtype(attn), _stream(stream)))
+
+
+def linear_bt(x, w, y, stream=None) -> None:
+    """y [M,N] = x [M,K] . w [N,K]^T."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError(f"shapes x {tuple(x.shape)}, w {tuple(w.shape)}, y {tuple(y.shape)}")
+    _check("linear_bt", lib().linear_bt(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dtype(x), _stream(stream)))
 
 
 _MASK_KINDS = {"sliding": 0, "csa": 1, "hca": 2}

@@ -119,6 +119,41 @@ int compressor_cache_update(const void* x_new, const void* gate_new, void* x_rin
                   "compressor_cache_update");
 }
 
+int linear_bt(const void* x, const void* w, void* y, int M, int N, int K, int dtype, void* stream) {
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(M >= 0 && N >= 1 && K >= 1, "M >= 0, N >= 1, K >= 1 required");
+  if (M == 0) return ok();
+  REQUIRE(x && w && y, "null x/w/y");
+  REQUIRE(aligned16(x) && aligned16(w) && aligned16(y), "pointers must be 16-byte aligned");
+  return launched(dsv4::launch_gemm_bt(x, w, y, M, N, K, K, K, N, 1, 0, 0, 0, dtype,
+                                       static_cast<hipStream_t>(stream)),
+                  "linear_bt");
+}
+
+int grouped_out_proj(const void* attn, const void* w_a, const void* w_b, void* mid, void* out, int T,
+                     int H, int D, int groups, int rank, int hidden, int dtype, void* stream) {
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(T >= 0 && H >= 1 && D >= 1 && rank >= 1 && hidden >= 1, "sizes must be positive");
+  REQUIRE(groups >= 1 && H % groups == 0, "groups %d must divide H=%d", groups, H);
+  if (static_cast<long long>(T) * H * D * 2 >= (1LL << 31) ||
+      static_cast<long long>(T) * groups * rank * 2 >= (1LL << 31) ||
+      static_cast<long long>(T) * hidden * 2 >= (1LL << 31))
+    return fail(DSV4_ERR_UNSUPPORTED, "a [T, .] operand of 2 GiB or more: split T");
+  if (T == 0) return ok();
+  REQUIRE(attn && w_a && w_b && mid && out, "null attn/w_a/w_b/mid/out");
+  REQUIRE(aligned16(attn) && aligned16(w_a) && aligned16(w_b) && aligned16(mid) && aligned16(out),
+          "pointers must be 16-byte aligned");
+  const long long kg = static_cast<long long>(H / groups) * D;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dsv4::launch_gemm_bt(attn, w_a, mid, T, rank, static_cast<int>(kg), static_cast<long long>(H) * D,
+                                      kg, static_cast<long long>(groups) * rank, groups, kg, rank * kg, rank,
+                                      dtype, st);
+  if (e != hipSuccess) return launched(e, "grouped_out_proj (o_a)");
+  return launched(dsv4::launch_gemm_bt(mid, w_b, out, T, hidden, groups * rank, static_cast<long long>(groups) * rank,
+                                       static_cast<long long>(groups) * rank, hidden, 1, 0, 0, 0, dtype, st),
+                  "grouped_out_proj (o_b)");
+}
+
 int attention_mask_dump(int kind, int S, int window, int m, const int* topk_idx, int k,
                         int n_entries, long long q_pos0, int format, char* buf, size_t buf_bytes,
                         size_t* needed) {

@@ -72,6 +72,12 @@ bool attend_uses_fast(const AttendArgs& a);
 // Keys one query may see at most (sizes the generic attention kernel's LDS).
 int attend_generic_max_keys();
 
+// C[M,N] = A[M,K] . B[N,K]^T per batch entry g (A, B, C offset by g * sA, sB, sC elements).
+hipError_t launch_gemm_bt(const void* A, const void* B, void* C, int M, int N, int K, long long lda,
+                          long long ldb, long long ldc, int batch, long long sA, long long sB, long long sC,
+                          int dtype, hipStream_t st);
+bool gemm_fast(int N, int K, long long lda, long long ldb, long long ldc, int dtype);
+
 // Visibility rendering of one layer (host only).  kind 0 sliding, 1 CSA, 2 HCA; format 0 text,
 // 1 ANSI text, 2 SVG, 3 per-query index lists.  topk_idx: host [S][k] (CSA).
 struct MaskDumpArgs {

@@ -153,3 +153,20 @@ def test_cache_update_argument_errors(lib):
     assert call(m=2049) == UNSUPPORTED                        # ring of 2m rows above 4096
     assert call(B=0) == OK and lib.dsv4_last_error() == b""
     assert call() == INVALID and b"null" in lib.dsv4_last_error()
+
+
+def test_projection_argument_errors(lib):
+    def op(**kw):
+        a = dict(T=16, H=64, D=512, G=8, rank=1024, hidden=4096, dtype=BF16)
+        a.update(kw)
+        return lib.grouped_out_proj(None, None, None, None, None, a["T"], a["H"], a["D"], a["G"],
+                                    a["rank"], a["hidden"], a["dtype"], None)
+    assert op(G=3) == INVALID and b"divide" in lib.dsv4_last_error()
+    assert op(rank=0) == INVALID
+    assert op(dtype=9) == INVALID
+    assert op(T=40000) == UNSUPPORTED                         # [T, H*D] bf16 beyond 2 GiB
+    assert op(T=0) == OK
+    assert op() == INVALID and b"null" in lib.dsv4_last_error()
+    assert lib.linear_bt(None, None, None, 4, 0, 8, BF16, None) == INVALID
+    assert lib.linear_bt(None, None, None, 0, 8, 8, BF16, None) == OK
+    assert lib.linear_bt(None, None, None, 4, 8, 8, BF16, None) == INVALID

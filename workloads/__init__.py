@@ -104,11 +104,14 @@ class Workload:
     n_seq: int = 0  # decode: number of sequences
     L_min: int = 0
     L_max: int = 0
+    o_groups: int = 8  # grouped output projection: head groups
+    o_rank: int = 1024  # o_lora_rank
+    hidden: int = 4096  # hidden_size
 
 
 WORKLOADS: Dict[int, Workload] = {
     1: Workload(1, "tiny_csa_fp32_S256", "fp32", 1, 256, 8, 64, 16, 4, 128, 4, 32, 16, 32,
-                10000.0, 0, "csa"),
+                10000.0, 0, "csa", o_groups=4, o_rank=32, hidden=64),
     2: Workload(2, "csa_prefill_bf16_S8192", "bf16", 1, 8192, 64, 512, 64, 4, 128, 64, 128, 512,
                 128, 10000.0, 2, "csa"),
     3: Workload(3, "hca_prefill_bf16_S65536", "bf16", 1, 65536, 64, 512, 64, 4, 128, 64, 128,
@@ -339,3 +342,25 @@ def random_index_lists(seed: int, name: str, B: int, T: int, k: int, N: int,
             if shuffle:
                 gen.shuffle(out[b, t])
     return out
+
+
+# ----------------------------------------------------------------------------
+# grouped output projection inputs
+# ----------------------------------------------------------------------------
+
+
+def oproj_inputs(w: Workload, T: Optional[int] = None, rows=None, layer: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of the grouped output projection: ``attn`` [T, H, D] standing for the attention
+    output, N(0, 1); ``w_a`` [o_groups, o_rank, H/o_groups * D] ~ N(0, 1/fan_in) and ``w_b``
+    [hidden, o_groups * o_rank] ~ N(0, 1/fan_in), the fan-in scaling of a linear layer's
+    initialisation (no trained weights exist here).  ``rows`` selects token rows of attn (their
+    values do not depend on which others are drawn)."""
+    T = w.S * w.B if T is None else T
+    kg = w.H // w.o_groups * w.D
+    rsel = slice(0, T) if rows is None else rows
+    attn = normal_rows(w.seed, layer, "o_attn", (w.H, w.D), rsel, T)
+    wa = normal_tensor(w.seed, layer, "w_oa", (w.o_groups * w.o_rank, kg)) / np.sqrt(kg)
+    wb = normal_tensor(w.seed, layer, "w_ob", (w.hidden, w.o_groups * w.o_rank)) / np.sqrt(w.o_groups * w.o_rank)
+    return {"attn": encode(attn, w.dtype),
+            "w_a": encode(wa.astype(np.float32).reshape(w.o_groups, w.o_rank, kg), w.dtype),
+            "w_b": encode(wb.astype(np.float32), w.dtype)}
