@@ -20,7 +20,8 @@ stated storage types (pool, indexer keys and the rotated window are stored in bf
 Parity status per function (what pins it, see tests/test_oracle_pins.py):
   rope                     pinned: isometry, composition, identity at 0, closed-form angle
   compress                 pinned: mean pooling, one-hot copy, window geometry, known weights,
-                           permutation invariance.  Exact gate/bias form (R1) is a reading:
+                           permutation invariance; the R4b variant: equal to R4 when both
+                           projections agree, half locality, one-hot copy from each half.  Exact gate/bias form (R1) is a reading:
                            the page prints no compressor formula, so its constants are
                            parity unpinned by the page itself.
   index_scores             pinned: single-head closed form, head additivity, ReLU cut-off.
@@ -101,7 +102,8 @@ def rope(x: np.ndarray, pos, rope_dim: int, base: float) -> np.ndarray:
 
 def compress(x: np.ndarray, gate: np.ndarray, bias: Optional[np.ndarray], m: int, overlap: bool,
              rope_dim: int = 0, base: float = 10000.0, pos_offset: int = 0,
-             entry_begin: int = 0, entry_end: Optional[int] = None) -> np.ndarray:
+             entry_begin: int = 0, entry_end: Optional[int] = None,
+             x_prev: Optional[np.ndarray] = None, gate_prev: Optional[np.ndarray] = None) -> np.ndarray:
     """Pool tokens [S, C] into compressed entries [N, C], N = S // m.
 
     "Hybrid attention (§2.3)": CSA pools at rate m with overlapping windows, HCA at rate m'
@@ -116,10 +118,18 @@ def compress(x: np.ndarray, gate: np.ndarray, bias: Optional[np.ndarray], m: int
          HCA window: tokens [w m, (w+1) m) (m slots).
       R3 a trailing partial window (S mod m tokens) emits no entry.
       R5 RoPE (rope_dim > 0) after pooling, at position (w+1)m - 1 + pos_offset.
+      R4 one token projection (x, gate) serves both halves of a CSA window.  Variant R4b
+         ("separate-projection overlap halves"): with x_prev / gate_prev given, the earlier
+         half (slots 0..m-1, tokens (w-1)m .. wm-1) takes its values and gates from them and
+         the later half from x / gate; one softmax still spans all 2m slots.
     Returns entries [entry_begin, entry_end) as rows of an [entry_end - entry_begin, C] array.
     """
     x = np.asarray(x, dtype=np.float64)
     g = np.asarray(gate, dtype=np.float64)
+    split = overlap and x_prev is not None
+    if split:
+        xp = np.asarray(x_prev, dtype=np.float64)
+        gp = np.asarray(gate_prev, dtype=np.float64)
     S, C = x.shape
     N = S // m
     entry_end = N if entry_end is None else entry_end
@@ -131,12 +141,18 @@ def compress(x: np.ndarray, gate: np.ndarray, bias: Optional[np.ndarray], m: int
         js = [j for j in range(lo, lo + span) if 0 <= j < S]
         slots = [j - lo for j in js]
         a = g[js].copy()
+        xs = x[js]
+        if split:  # the earlier half's slots read the second projection
+            early = np.array([s_ < m for s_ in slots])
+            a[early] = gp[js][early]
+            xs = xs.copy()
+            xs[early] = xp[js][early]
         if bias is not None:
             a += np.asarray(bias, dtype=np.float64)[slots]
         a -= a.max(axis=0, keepdims=True)
         e = np.exp(a)
         pi = e / e.sum(axis=0, keepdims=True)
-        out[w - entry_begin] = (pi * x[js]).sum(axis=0)
+        out[w - entry_begin] = (pi * xs).sum(axis=0)
     if rope_dim:
         pos = (np.arange(entry_begin, entry_end) + 1) * m - 1 + pos_offset
         out = rope(out, pos, rope_dim, base)
@@ -246,11 +262,15 @@ def attend_query(q_t: np.ndarray, keys: np.ndarray, sink: np.ndarray, p_t: float
 
 
 def csa_compress(x, gate, bias, m, overlap, rope_dim=0, base=10000.0, pos_offset=0,
-                 entry_begin=0, entry_end=None):
-    """Batched compress: x, gate [B, S, C] -> pool rows [B, entry_end - entry_begin, C]."""
+                 entry_begin=0, entry_end=None, x_prev=None, gate_prev=None):
+    """Batched compress: x, gate [B, S, C] -> pool rows [B, entry_end - entry_begin, C];
+    x_prev, gate_prev [B, S, C] select the R4b variant."""
     x = np.asarray(x)
     return np.stack([compress(x[b], gate[b], bias, m, overlap, rope_dim, base, pos_offset,
-                              entry_begin, entry_end) for b in range(x.shape[0])])
+                              entry_begin, entry_end,
+                              None if x_prev is None else x_prev[b],
+                              None if gate_prev is None else gate_prev[b])
+                     for b in range(x.shape[0])])
 
 
 def swa_concat(kv_raw, new_pos0, rope_dim, base, pos_offset=0):

@@ -419,6 +419,36 @@ def pin_round_bf16(O):
 
 
 # ----------------------------------------------------------------------------
+# compressor variant R4b: separate projections for the two halves of a CSA window
+# ----------------------------------------------------------------------------
+
+
+def pin_compress_split_halves(O):
+    """R4b reduces to R4 when both projections agree; the earlier half reads only the second
+    projection and the later half only the first; a dominant gate copies one slot's value."""
+    r = RNG(31)
+    S, C, m = 21, 5, 4
+    x, g = r.standard_normal((S, C)), r.standard_normal((S, C))
+    bias = r.standard_normal((2 * m, C))
+    same = O.compress(x, g, bias, m, True, x_prev=x, gate_prev=g)
+    _close(same, O.compress(x, g, bias, m, True), 0.0, "R4b with equal projections")
+    xp, gp = r.standard_normal((S, C)), r.standard_normal((S, C))
+    base = O.compress(x, g, bias, m, True, x_prev=xp, gate_prev=gp)
+    w = 3  # tokens 8..11 form its earlier half, 12..15 its later half
+    x2 = x.copy(); x2[8:12] += 5.0; g2 = g.copy(); g2[8:12] -= 3.0
+    _close(O.compress(x2, g2, bias, m, True, x_prev=xp, gate_prev=gp)[w], base[w], 0.0,
+           "earlier half ignores the first projection")
+    xp2 = xp.copy(); xp2[12:16] += 5.0; gp2 = gp.copy(); gp2[12:16] -= 3.0
+    _close(O.compress(x, g, bias, m, True, x_prev=xp2, gate_prev=gp2)[w], base[w], 0.0,
+           "later half ignores the second projection")
+    for j, src in ((9, "prev"), (14, "cur")):
+        gq, gpq = np.zeros((S, C)), np.zeros((S, C))
+        (gpq if src == "prev" else gq)[j] = 80.0
+        e = O.compress(x, gq, None, m, True, x_prev=xp, gate_prev=gpq)[w]
+        _close(e, (xp if src == "prev" else x)[j], 1e-12, f"one-hot slot {j} from {src}")
+
+
+# ----------------------------------------------------------------------------
 # grouped output projection
 # ----------------------------------------------------------------------------
 

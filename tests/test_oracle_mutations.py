@@ -51,6 +51,8 @@ MUTATIONS = {
                                    "s = np.asarray(scores, dtype=np.float64)"),
                                   ("key=lambda w: (-s[w], w)",
                                    "key=lambda w: (-s[w], 0 if np.signbit(s[w]) else -1, w)")],
+    "split_halves_swapped": [("early = np.array([s_ < m for s_ in slots])",
+                              "early = np.array([s_ >= m for s_ in slots])")],
     "oproj_heads_interleaved": [("mid[:, g * rank:(g + 1) * rank] = a[:, g * kg:(g + 1) * kg] @ w_a[g].T",
                                  "mid[:, g * rank:(g + 1) * rank] = "
                                  "np.asarray(attn, dtype=np.float64)[:, g::groups].reshape(T, -1) @ w_a[g].T")],
