@@ -112,6 +112,35 @@ int compressor_cache_update(const void* x_new, const void* gate_new, void* x_rin
                             void* stream);
 
 /*
+ * csa_compress_split - csa_compress with separate projections for the two halves of each
+ * overlapping window (reading R4b of the CSA compressor: the earlier half of entry w's window,
+ * tokens (w-1)m .. wm-1, takes its values and gates from x_prev / gate_prev, the later half,
+ * wm .. (w+1)m-1, from x / gate; one softmax spans all 2m slots).  Always overlapping.
+ *
+ *   x_prev, gate_prev : [B, S, C] dtype, both given or both NULL (NULL = csa_compress with
+ *     overlap = 1).  Every other argument as csa_compress.
+ */
+int csa_compress_split(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
+                       const float* bias, void* pool, int B, int S, int C, int m, int entry_begin,
+                       int entry_end, int N_cap, int rope_dim, double rope_theta,
+                       long long rope_pos_offset, int dtype, void* stream);
+
+/*
+ * compressor_cache_update_split - compressor_cache_update for the R4b compressor (overlapping
+ * windows, separate projections for the two halves): the new token's second projection
+ * (x_prev_new, gate_prev_new [B, C]) goes into its own rings (x_prev_ring, gate_prev_ring
+ * [B, 2m, C], slot (L-1) mod 2m like the first), and a closing entry pools its earlier half
+ * from them.  All four second-projection pointers are required; the rest as
+ * compressor_cache_update with overlap = 1.
+ */
+int compressor_cache_update_split(const void* x_new, const void* gate_new, const void* x_prev_new,
+                                  const void* gate_prev_new, void* x_ring, void* gate_ring,
+                                  void* x_prev_ring, void* gate_prev_ring, const float* bias,
+                                  void* pool, const int* lengths, int B, int C, int m, int N_cap,
+                                  int rope_dim, double rope_theta, long long rope_pos_offset,
+                                  int emit, int dtype, void* stream);
+
+/*
  * csa_index_topk - Lightning Indexer scores and top-k per query ("Hybrid attention (§2.3)",
  * CSA item, eqs. 13-17; "Attention mask layout", CSA paragraph for the -1 sentinel;
  * "DeepseekV4Config": index_n_heads, index_head_dim, index_topk).

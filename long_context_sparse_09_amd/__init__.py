@@ -70,14 +70,24 @@ def _check(fn: str, status: int) -> None:
 
 def csa_compress(x, gate, bias, pool, m: int, overlap: bool, entry_begin: int = 0,
                  entry_end: Optional[int] = None, rope_dim: int = 0, rope_theta: float = 10000.0,
-                 rope_pos_offset: int = 0, stream=None) -> None:
-    """x, gate [B,S,C]; bias [2m or m, C] fp32 or None; pool [B,N_cap,C] (rows written)."""
+                 rope_pos_offset: int = 0, stream=None, x_prev=None, gate_prev=None) -> None:
+    """x, gate [B,S,C]; bias [2m or m, C] fp32 or None; pool [B,N_cap,C] (rows written).
+    x_prev, gate_prev [B,S,C]: the second projection of the earlier window halves (overlap
+    only; calls csa_compress_split)."""
     B, S, C = x.shape
     N_cap = pool.shape[1]
     if bias is not None and tuple(bias.shape) != ((2 * m if overlap else m), C):
         raise ValueError(f"bias must be [{2 * m if overlap else m}, {C}], got {tuple(bias.shape)}")
     if entry_end is None:
         entry_end = min(S // m, N_cap)
+    if x_prev is not None or gate_prev is not None:
+        if not overlap:
+            raise ValueError("a second projection needs overlapping windows")
+        _check("csa_compress_split", lib().csa_compress_split(
+            _ptr(x), _ptr(gate), _ptr(x_prev), _ptr(gate_prev), _ptr(bias), _ptr(pool), B, S, C, m,
+            entry_begin, entry_end, N_cap, rope_dim, float(rope_theta), int(rope_pos_offset),
+            _dtype(x), _stream(stream)))
+        return
     _check("csa_compress", lib().csa_compress(
         _ptr(x), _ptr(gate), _ptr(bias), _ptr(pool), B, S, C, m, int(bool(overlap)), entry_begin,
         entry_end, N_cap, rope_dim, float(rope_theta), int(rope_pos_offset), _dtype(x),
@@ -86,11 +96,23 @@ def csa_compress(x, gate, bias, pool, m: int, overlap: bool, entry_begin: int = 
 
 def compressor_cache_update(x_new, gate_new, x_ring, gate_ring, bias, pool, lengths, m: int,
                             overlap: bool, rope_dim: int = 0, rope_theta: float = 10000.0,
-                            rope_pos_offset: int = 0, emit: bool = True, stream=None) -> None:
+                            rope_pos_offset: int = 0, emit: bool = True, stream=None,
+                            x_prev_new=None, gate_prev_new=None, x_prev_ring=None,
+                            gate_prev_ring=None) -> None:
     """x_new, gate_new [B,C]; x_ring, gate_ring [B,span,C]; bias [span,C] fp32 or None;
-    pool [B,N_cap,C] (or None when emit is False); lengths [B] int32 (tokens incl. the new)."""
+    pool [B,N_cap,C] (or None when emit is False); lengths [B] int32 (tokens incl. the new).
+    The *_prev arguments (all four) select the second-projection compressor (overlap only)."""
     B, C = x_new.shape
     N_cap = 0 if pool is None else pool.shape[1]
+    if x_prev_new is not None:
+        if not overlap:
+            raise ValueError("a second projection needs overlapping windows")
+        _check("compressor_cache_update_split", lib().compressor_cache_update_split(
+            _ptr(x_new), _ptr(gate_new), _ptr(x_prev_new), _ptr(gate_prev_new), _ptr(x_ring),
+            _ptr(gate_ring), _ptr(x_prev_ring), _ptr(gate_prev_ring), _ptr(bias), _ptr(pool),
+            _ptr(lengths), B, C, m, N_cap, rope_dim, float(rope_theta), int(rope_pos_offset),
+            int(bool(emit)), _dtype(x_new), _stream(stream)))
+        return
     _check("compressor_cache_update", lib().compressor_cache_update(
         _ptr(x_new), _ptr(gate_new), _ptr(x_ring), _ptr(gate_ring), _ptr(bias), _ptr(pool),
         _ptr(lengths), B, C, m, int(bool(overlap)), N_cap, rope_dim, float(rope_theta),

@@ -28,6 +28,13 @@ SIGNATURES = {
     "linear_bt": ([c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p], c_int),
     "attention_mask_dump": ([c_int, c_int, c_int, c_int, c_void_p, c_int, c_int, c_ll, c_int,
                              c_char_p, c_size_t, ctypes.POINTER(c_size_t)], c_int),
+    "csa_compress_split": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                            c_int, c_int, c_int, c_int, c_int, c_int, c_double, c_ll, c_int,
+                            c_void_p], c_int),
+    "compressor_cache_update_split": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                       c_int, c_int, c_int, c_int, c_double, c_ll, c_int, c_int,
+                                       c_void_p], c_int),
     "csa_index_topk_workspace_size": ([c_int, c_int, c_int, c_int], c_size_t),
     "csa_index_topk": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_size_t,

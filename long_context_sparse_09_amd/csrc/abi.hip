@@ -67,10 +67,14 @@ const char* dsv4_status_string(int status) {
 
 const char* dsv4_last_error(void) { return g_last_error; }
 
-int csa_compress(const void* x, const void* gate, const float* bias, void* pool, int B, int S,
-                 int C, int m, int overlap, int entry_begin, int entry_end, int N_cap,
-                 int rope_dim, double rope_theta, long long rope_pos_offset, int dtype,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+int compress_common(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
+                    const float* bias, void* pool, int B, int S, int C, int m, int overlap, int entry_begin,
+                    int entry_end, int N_cap, int rope_dim, double rope_theta, long long rope_pos_offset,
+                    int dtype, void* stream, const char* name) {
   REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
   REQUIRE(B >= 0 && S >= 0 && N_cap >= 0, "negative size");
   REQUIRE(m >= 1, "m must be >= 1");
@@ -84,19 +88,18 @@ int csa_compress(const void* x, const void* gate, const float* bias, void* pool,
   if (int rc = check_rope(rope_dim, C, rope_theta)) return rc;
   if (B == 0 || entry_begin == entry_end) return ok();
   REQUIRE(x && gate && pool, "null x/gate/pool");
-  REQUIRE(aligned16(x) && aligned16(gate) && aligned16(pool) && (!bias || aligned16(bias)),
+  REQUIRE(aligned16(x) && aligned16(gate) && aligned16(pool) && (!bias || aligned16(bias)) &&
+              (!x_prev || aligned16(x_prev)) && (!gate_prev || aligned16(gate_prev)),
           "pointers must be 16-byte aligned");
-  return launched(dsv4::launch_compress(x, gate, bias, pool, B, S, C, m, overlap, entry_begin,
-                                        entry_end, N_cap, rope_dim, rope_theta, rope_pos_offset,
-                                        dtype, static_cast<hipStream_t>(stream)),
-                  "csa_compress");
+  return launched(dsv4::launch_compress(x, gate, x_prev, gate_prev, bias, pool, B, S, C, m, overlap, entry_begin,
+                                        entry_end, N_cap, rope_dim, rope_theta, rope_pos_offset, dtype,
+                                        static_cast<hipStream_t>(stream)),
+                  name);
 }
 
-int compressor_cache_update(const void* x_new, const void* gate_new, void* x_ring,
-                            void* gate_ring, const float* bias, void* pool, const int* lengths,
-                            int B, int C, int m, int overlap, int N_cap, int rope_dim,
-                            double rope_theta, long long rope_pos_offset, int emit, int dtype,
-                            void* stream) {
+int cache_update_common(const dsv4::CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int rope_dim,
+                        double rope_theta, long long rope_pos_offset, int emit, int dtype, void* stream,
+                        const char* name) {
   REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
   REQUIRE(B >= 0 && N_cap >= 0, "negative size");
   REQUIRE(m >= 1, "m must be >= 1");
@@ -107,16 +110,59 @@ int compressor_cache_update(const void* x_new, const void* gate_new, void* x_rin
   if ((overlap ? 2 * m : m) > 4096) return fail(DSV4_ERR_UNSUPPORTED, "window span above 4096");
   if (int rc = check_rope(rope_dim, C, rope_theta)) return rc;
   if (B == 0) return ok();
-  REQUIRE(x_new && gate_new && x_ring && gate_ring && lengths, "null required pointer");
-  REQUIRE(!emit || pool, "pool required when emitting entries");
-  REQUIRE(aligned16(x_new) && aligned16(gate_new) && aligned16(x_ring) && aligned16(gate_ring) &&
-              (!pool || aligned16(pool)) && (!bias || aligned16(bias)),
-          "pointers must be 16-byte aligned");
-  return launched(dsv4::launch_cache_update(x_new, gate_new, x_ring, gate_ring, bias, pool,
-                                            lengths, B, C, m, overlap, N_cap, rope_dim,
-                                            rope_theta, rope_pos_offset, emit, dtype,
-                                            static_cast<hipStream_t>(stream)),
-                  "compressor_cache_update");
+  REQUIRE(u.x_new && u.g_new && u.x_ring && u.g_ring && u.lengths, "null required pointer");
+  REQUIRE(!emit || u.pool, "pool required when emitting entries");
+  for (const void* p : {u.x_new, u.g_new, static_cast<const void*>(u.x_ring), static_cast<const void*>(u.g_ring),
+                        u.xp_new, u.gp_new, static_cast<const void*>(u.xp_ring), static_cast<const void*>(u.gp_ring),
+                        static_cast<const void*>(u.pool), static_cast<const void*>(u.bias)})
+    REQUIRE(!p || aligned16(p), "pointers must be 16-byte aligned");
+  return launched(dsv4::launch_cache_update(u, B, C, m, overlap, N_cap, rope_dim, rope_theta, rope_pos_offset, emit,
+                                            dtype, static_cast<hipStream_t>(stream)),
+                  name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_compress(const void* x, const void* gate, const float* bias, void* pool, int B, int S,
+                 int C, int m, int overlap, int entry_begin, int entry_end, int N_cap,
+                 int rope_dim, double rope_theta, long long rope_pos_offset, int dtype,
+                 void* stream) {
+  return compress_common(x, gate, nullptr, nullptr, bias, pool, B, S, C, m, overlap, entry_begin, entry_end,
+                         N_cap, rope_dim, rope_theta, rope_pos_offset, dtype, stream, "csa_compress");
+}
+
+int csa_compress_split(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
+                       const float* bias, void* pool, int B, int S, int C, int m, int entry_begin,
+                       int entry_end, int N_cap, int rope_dim, double rope_theta, long long rope_pos_offset,
+                       int dtype, void* stream) {
+  REQUIRE((x_prev == nullptr) == (gate_prev == nullptr), "x_prev and gate_prev go together");
+  return compress_common(x, gate, x_prev, gate_prev, bias, pool, B, S, C, m, 1, entry_begin, entry_end, N_cap,
+                         rope_dim, rope_theta, rope_pos_offset, dtype, stream, "csa_compress_split");
+}
+
+int compressor_cache_update(const void* x_new, const void* gate_new, void* x_ring,
+                            void* gate_ring, const float* bias, void* pool, const int* lengths,
+                            int B, int C, int m, int overlap, int N_cap, int rope_dim,
+                            double rope_theta, long long rope_pos_offset, int emit, int dtype,
+                            void* stream) {
+  const dsv4::CacheUpdate u{x_new, gate_new, x_ring, gate_ring, nullptr, nullptr, nullptr, nullptr, bias, pool,
+                            lengths};
+  return cache_update_common(u, B, C, m, overlap, N_cap, rope_dim, rope_theta, rope_pos_offset, emit, dtype,
+                             stream, "compressor_cache_update");
+}
+
+int compressor_cache_update_split(const void* x_new, const void* gate_new, const void* x_prev_new,
+                                  const void* gate_prev_new, void* x_ring, void* gate_ring, void* x_prev_ring,
+                                  void* gate_prev_ring, const float* bias, void* pool, const int* lengths, int B,
+                                  int C, int m, int N_cap, int rope_dim, double rope_theta,
+                                  long long rope_pos_offset, int emit, int dtype, void* stream) {
+  REQUIRE(x_prev_new && gate_prev_new && x_prev_ring && gate_prev_ring, "null second-projection pointer");
+  const dsv4::CacheUpdate u{x_new, gate_new, x_ring, gate_ring, x_prev_new, gate_prev_new, x_prev_ring,
+                            gate_prev_ring, bias, pool, lengths};
+  return cache_update_common(u, B, C, m, 1, N_cap, rope_dim, rope_theta, rope_pos_offset, emit, dtype, stream,
+                             "compressor_cache_update_split");
 }
 
 int linear_bt(const void* x, const void* w, void* y, int M, int N, int K, int dtype, void* stream) {

@@ -23,9 +23,10 @@ namespace dsv4 {
 // ---------------------------------------------------------------------------
 template <typename T, int VEC>
 __global__ void __launch_bounds__(256) compress_kernel(
-    const T* __restrict__ x, const T* __restrict__ gate, const float* __restrict__ bias,
-    T* __restrict__ pool, int S, int C, int m, int overlap, int e0, int e1, int N_cap, int r,
-    const RopeFreq rf, long long pos_off, int G, int P, int E) {
+    const T* __restrict__ x, const T* __restrict__ gate, const T* __restrict__ x_prev,
+    const T* __restrict__ gate_prev, const float* __restrict__ bias, T* __restrict__ pool, int S,
+    int C, int m, int overlap, int e0, int e1, int N_cap, int r, const RopeFreq rf, long long pos_off,
+    int G, int P, int E) {
   extern __shared__ float red[];  // [E*P*G][3*VEC] partial states when P > 1
   __shared__ double inv_freq[kMaxRope / 2];
   for (int i = threadIdx.x; i < r / 2; i += blockDim.x) inv_freq[i] = rf.inv[i];
@@ -61,8 +62,10 @@ __global__ void __launch_bounds__(256) compress_kernel(
         const int j = lo + s;
         ok[u] = s < s1 && j >= 0 && j < S;
         const size_t jr = row0 + (ok[u] ? j : 0);  // a valid row; unused when !ok
-        Chunk<T>::template load<VEC>(x + jr * C + c0, xv[u]);
-        Chunk<T>::template load<VEC>(gate + jr * C + c0, gv[u]);
+        // the earlier half of a window reads the second projection when one is given
+        const bool early = x_prev != nullptr && s < m;
+        Chunk<T>::template load<VEC>((early ? x_prev : x) + jr * C + c0, xv[u]);
+        Chunk<T>::template load<VEC>((early ? gate_prev : gate) + jr * C + c0, gv[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -123,9 +126,9 @@ __global__ void __launch_bounds__(256) compress_kernel(
 }
 
 template <typename T, int VEC>
-static hipError_t compress_t(const void* x, const void* gate, const float* bias, void* pool, int B,
-                             int S, int C, int m, int overlap, int e0, int e1, int N_cap, int r,
-                             double theta, long long off, hipStream_t st) {
+static hipError_t compress_t(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
+                             const float* bias, void* pool, int B, int S, int C, int m, int overlap, int e0,
+                             int e1, int N_cap, int r, double theta, long long off, hipStream_t st) {
   const int G = C / VEC;
   const int span = overlap ? 2 * m : m;
   // long windows: split the slots over P thread groups (16+ slots each)
@@ -138,22 +141,28 @@ static hipError_t compress_t(const void* x, const void* gate, const float* bias,
   dim3 grid(div_up(n, E), B);
   size_t shmem = P > 1 ? static_cast<size_t>(threads) * 3 * VEC * sizeof(float) : 0;
   hipLaunchKernelGGL((compress_kernel<T, VEC>), grid, dim3(threads), shmem, st,
-                     static_cast<const T*>(x), static_cast<const T*>(gate), bias,
-                     static_cast<T*>(pool), S, C, m, overlap, e0, e1, N_cap, r,
+                     static_cast<const T*>(x), static_cast<const T*>(gate), static_cast<const T*>(x_prev),
+                     static_cast<const T*>(gate_prev), bias, static_cast<T*>(pool), S, C, m, overlap, e0, e1,
+                     N_cap, r,
                      make_rope_freq(r, theta), off, G, P, E);
   return hipGetLastError();
 }
 
-hipError_t launch_compress(const void* x, const void* gate, const float* bias, void* pool, int B,
-                           int S, int C, int m, int overlap, int e0, int e1, int N_cap, int r,
-                           double theta, long long off, int dtype, hipStream_t st) {
+hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
+                           const float* bias, void* pool, int B, int S, int C, int m, int overlap, int e0,
+                           int e1, int N_cap, int r, double theta, long long off, int dtype, hipStream_t st) {
   const bool v8 = (C % 8 == 0) && (C / 8 <= 256);
+  if (!overlap) x_prev = gate_prev = nullptr;  // no earlier half
   if (dtype == 1) {
-    return v8 ? compress_t<bf16_t, 8>(x, gate, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r, theta, off, st)
-              : compress_t<bf16_t, 2>(x, gate, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r, theta, off, st);
+    return v8 ? compress_t<bf16_t, 8>(x, gate, x_prev, gate_prev, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r,
+                                      theta, off, st)
+              : compress_t<bf16_t, 2>(x, gate, x_prev, gate_prev, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r,
+                                      theta, off, st);
   }
-  return v8 ? compress_t<float, 8>(x, gate, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r, theta, off, st)
-            : compress_t<float, 2>(x, gate, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r, theta, off, st);
+  return v8 ? compress_t<float, 8>(x, gate, x_prev, gate_prev, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r,
+                                   theta, off, st)
+            : compress_t<float, 2>(x, gate, x_prev, gate_prev, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r,
+                                   theta, off, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -168,6 +177,7 @@ hipError_t launch_compress(const void* x, const void* gate, const float* bias, v
 template <typename T, int VEC>
 __global__ void __launch_bounds__(256) cache_update_kernel(
     const T* __restrict__ x_new, const T* __restrict__ g_new, T* x_ring, T* g_ring,
+    const T* __restrict__ xp_new, const T* __restrict__ gp_new, T* xp_ring, T* gp_ring,
     const float* __restrict__ bias, T* __restrict__ pool, const int* __restrict__ lengths, int C,
     int m, int overlap, int N_cap, int r, const RopeFreq rf, long long pos_off, int emit) {
   __shared__ double inv_freq[kMaxRope / 2];
@@ -190,6 +200,12 @@ __global__ void __launch_bounds__(256) cache_update_kernel(
     Chunk<T>::template store<VEC>(x_ring + (ring0 + slot) * C + c0, v);
     Chunk<T>::template load<VEC>(g_new + static_cast<size_t>(b) * C + c0, v);
     Chunk<T>::template store<VEC>(g_ring + (ring0 + slot) * C + c0, v);
+    if (xp_ring != nullptr) {  // the second projection, for the windows this token starts
+      Chunk<T>::template load<VEC>(xp_new + static_cast<size_t>(b) * C + c0, v);
+      Chunk<T>::template store<VEC>(xp_ring + (ring0 + slot) * C + c0, v);
+      Chunk<T>::template load<VEC>(gp_new + static_cast<size_t>(b) * C + c0, v);
+      Chunk<T>::template store<VEC>(gp_ring + (ring0 + slot) * C + c0, v);
+    }
     if (!closes) continue;
     float mx[VEC], sm[VEC], acc[VEC];
 #pragma unroll
@@ -199,8 +215,9 @@ __global__ void __launch_bounds__(256) cache_update_kernel(
       if (p < 0) continue;
       const size_t row = ring0 + p % span;
       float xv[VEC], gv[VEC];
-      Chunk<T>::template load<VEC>(x_ring + row * C + c0, xv);
-      Chunk<T>::template load<VEC>(g_ring + row * C + c0, gv);
+      const bool early = xp_ring != nullptr && s < m;  // the earlier half's second projection
+      Chunk<T>::template load<VEC>((early ? xp_ring : x_ring) + row * C + c0, xv);
+      Chunk<T>::template load<VEC>((early ? gp_ring : g_ring) + row * C + c0, gv);
       if (bias != nullptr) {
         float bv[VEC];
         Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s) * C + c0, bv);
@@ -231,30 +248,29 @@ __global__ void __launch_bounds__(256) cache_update_kernel(
 }
 
 template <typename T, int VEC>
-static hipError_t cache_update_t(const void* x_new, const void* g_new, void* x_ring, void* g_ring,
-                                 const float* bias, void* pool, const int* lengths, int B, int C,
-                                 int m, int overlap, int N_cap, int r, double theta, long long off,
-                                 int emit, hipStream_t st) {
+static hipError_t cache_update_t(const CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int r,
+                                 double theta, long long off, int emit, hipStream_t st) {
   const int G = C / VEC;
   const int threads = G >= 256 ? 256 : ((G + 63) / 64) * 64;
   hipLaunchKernelGGL((cache_update_kernel<T, VEC>), dim3(B), dim3(threads), 0, st,
-                     static_cast<const T*>(x_new), static_cast<const T*>(g_new),
-                     static_cast<T*>(x_ring), static_cast<T*>(g_ring), bias, static_cast<T*>(pool),
-                     lengths, C, m, overlap, N_cap, r, make_rope_freq(r, theta), off, emit);
+                     static_cast<const T*>(u.x_new), static_cast<const T*>(u.g_new), static_cast<T*>(u.x_ring),
+                     static_cast<T*>(u.g_ring), static_cast<const T*>(u.xp_new), static_cast<const T*>(u.gp_new),
+                     static_cast<T*>(u.xp_ring), static_cast<T*>(u.gp_ring), u.bias, static_cast<T*>(u.pool),
+                     u.lengths, C, m, overlap, N_cap, r, make_rope_freq(r, theta), off, emit);
   return hipGetLastError();
 }
 
-hipError_t launch_cache_update(const void* x_new, const void* g_new, void* x_ring, void* g_ring,
-                               const float* bias, void* pool, const int* lengths, int B, int C,
-                               int m, int overlap, int N_cap, int r, double theta, long long off,
-                               int emit, int dtype, hipStream_t st) {
+hipError_t launch_cache_update(const CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int r,
+                               double theta, long long off, int emit, int dtype, hipStream_t st) {
   if (B == 0) return hipSuccess;
+  CacheUpdate v = u;
+  if (!overlap || v.xp_ring == nullptr) v.xp_new = v.gp_new = v.xp_ring = v.gp_ring = nullptr;
   const bool v8 = (C % 8 == 0) && (C / 8 <= 256);
   if (dtype == 1)
-    return v8 ? cache_update_t<bf16_t, 8>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st)
-              : cache_update_t<bf16_t, 2>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st);
-  return v8 ? cache_update_t<float, 8>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st)
-            : cache_update_t<float, 2>(x_new, g_new, x_ring, g_ring, bias, pool, lengths, B, C, m, overlap, N_cap, r, theta, off, emit, st);
+    return v8 ? cache_update_t<bf16_t, 8>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st)
+              : cache_update_t<bf16_t, 2>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st);
+  return v8 ? cache_update_t<float, 8>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st)
+            : cache_update_t<float, 2>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -8,14 +8,29 @@
 
 namespace dsv4 {
 
-hipError_t launch_compress(const void* x, const void* gate, const float* bias, void* pool, int B,
-                           int S, int C, int m, int overlap, int e0, int e1, int N_cap, int r,
-                           double theta, long long off, int dtype, hipStream_t st);
+// x_prev / gate_prev: NULL, or the second projection the earlier half of each overlapping
+// window reads (overlap only).
+hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
+                           const float* bias, void* pool, int B, int S, int C, int m, int overlap, int e0,
+                           int e1, int N_cap, int r, double theta, long long off, int dtype, hipStream_t st);
 
-hipError_t launch_cache_update(const void* x_new, const void* g_new, void* x_ring, void* g_ring,
-                               const float* bias, void* pool, const int* lengths, int B, int C,
-                               int m, int overlap, int N_cap, int r, double theta, long long off,
-                               int emit, int dtype, hipStream_t st);
+// Decode-time compressor state: new token rows, rings of the last span tokens, pool.  The
+// xp_* / gp_* members are the second projection (NULL: one projection for both halves).
+struct CacheUpdate {
+  const void* x_new;
+  const void* g_new;
+  void* x_ring;
+  void* g_ring;
+  const void* xp_new;
+  const void* gp_new;
+  void* xp_ring;
+  void* gp_ring;
+  const float* bias;
+  void* pool;
+  const int* lengths;
+};
+hipError_t launch_cache_update(const CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int r,
+                               double theta, long long off, int emit, int dtype, hipStream_t st);
 
 hipError_t launch_swa(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0,
                       int B, int S_new, int S_cap, int D, int r, double theta, long long off,

@@ -170,3 +170,16 @@ def test_projection_argument_errors(lib):
     assert lib.linear_bt(None, None, None, 4, 0, 8, BF16, None) == INVALID
     assert lib.linear_bt(None, None, None, 0, 8, 8, BF16, None) == OK
     assert lib.linear_bt(None, None, None, 4, 8, 8, BF16, None) == INVALID
+
+
+def test_split_compressor_argument_errors(lib):
+    one = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert lib.csa_compress_split(None, None, one, None, None, None, 1, 64, 512, 4, 0, 16, 16, 64,
+                                  1e4, 0, BF16, None) == INVALID
+    assert b"together" in lib.dsv4_last_error()
+    assert lib.csa_compress_split(None, None, None, None, None, None, 0, 64, 512, 4, 0, 16, 16, 64,
+                                  1e4, 0, BF16, None) == OK            # B = 0: nothing to do
+    assert lib.compressor_cache_update_split(None, None, None, None, None, None, None, None, None,
+                                             None, None, 2, 512, 4, 64, 64, 1e4, 0, 1, BF16,
+                                             None) == INVALID
+    assert b"second-projection" in lib.dsv4_last_error()

@@ -70,6 +70,70 @@ def test_csa_compress(case):
         assert_bf16_ulp(got[:, e0:e1], ref, "pool")
 
 
+SPLIT_CASES = [
+    # dtype, B, S, C, m, rope, bias, entries
+    ("fp32", 1, 259, 64, 4, 16, True, None),
+    ("bf16", 2, 1030, 512, 4, 64, True, None),
+    ("bf16", 1, 1030, 128, 4, 0, True, (30, 200)),
+    ("bf16", 1, 700, 512, 128, 64, False, None),      # long windows: slots split over thread groups
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "-".join(map(str, c[:6])))
+def test_csa_compress_split_halves(case):
+    """R4b: the earlier half of every overlapping window reads the second projection."""
+    dt, B, S, C, m, r, use_bias, entries = case
+    x, g = normal("x", (B, S, C)), normal("g", (B, S, C))
+    xp, gp = normal("xp", (B, S, C)), normal("gp", (B, S, C))
+    bias = normal("bias", (2 * m, C)).astype(np.float32) if use_bias else None
+    enc4 = [enc(a, dt) for a in (x, g, xp, gp)]
+    N = S // m
+    e0, e1 = entries if entries else (0, N)
+    pool = torch.full((B, N, C), 7.0, dtype=torch_dtype(dt), device="cuda")
+    L.csa_compress(dev(enc4[0]), dev(enc4[1]), None if bias is None else dev(bias), pool, m, True, e0, e1,
+                   r, 10000.0, 5, x_prev=dev(enc4[2]), gate_prev=dev(enc4[3]))
+    got = host(pool)
+    x64, g64, xp64, gp64 = (W.to_f64(a) for a in enc4)
+    ref = oracle.csa_compress(x64, g64, None if bias is None else bias.astype(np.float64), m, True, r,
+                              10000.0, 5, e0, e1, x_prev=xp64, gate_prev=gp64)
+    assert np.all(got[:, :e0] == 7.0) and np.all(got[:, e1:] == 7.0), "rows outside the range"
+    assert_close(got[:, e0:e1], ref, dt, "pool (split halves)")
+    if dt == "bf16":
+        assert_bf16_ulp(got[:, e0:e1], ref, "pool (split halves)")
+
+
+def test_cache_update_split_halves_decode():
+    """Token-by-token decode of the R4b compressor: rings of both projections, an entry
+    closed every m tokens, sequences of different lengths (a finished sequence gets length 0
+    and is left alone), against the oracle's pool of each whole history."""
+    B, C, m, r = 3, 128, 4, 16
+    S_b = [23, 30, 9]
+    S = max(S_b)
+    x, g = normal("x", (B, S, C)), normal("g", (B, S, C))
+    xp, gp = normal("xp", (B, S, C)), normal("gp", (B, S, C))
+    bias = normal("bias", (2 * m, C)).astype(np.float32)
+    e = [enc(a, "bf16") for a in (x, g, xp, gp)]
+    N_cap = S // m
+    rings = [torch.zeros(B, 2 * m, C, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    pool = torch.zeros(B, N_cap, C, dtype=torch.bfloat16, device="cuda")
+    for t in range(S):
+        lens = np.array([t + 1 if t < S_b[b] else 0 for b in range(B)], dtype=np.int32)
+        tok = [np.ascontiguousarray(a[:, t]) for a in e]
+        L.compressor_cache_update(dev(tok[0]), dev(tok[1]), rings[0], rings[1], dev(bias), pool,
+                                  i32(lens), m, True, r, 10000.0, 0, emit=True,
+                                  x_prev_new=dev(tok[2]), gate_prev_new=dev(tok[3]),
+                                  x_prev_ring=rings[2], gate_prev_ring=rings[3])
+    torch.cuda.synchronize()
+    got = host(pool)
+    for b in range(B):
+        n = S_b[b] // m
+        x64, g64, xp64, gp64 = (W.to_f64(a[b:b + 1, :S_b[b]]) for a in e)
+        ref = oracle.csa_compress(x64, g64, bias.astype(np.float64), m, True, r, 10000.0, 0,
+                                  x_prev=xp64, gate_prev=gp64)[0]
+        assert_bf16_ulp(got[b, :n], ref, f"pool from decode (split halves), sequence {b}")
+        assert np.all(got[b, n:] == 0.0), "entries beyond the sequence's closed windows"
+
+
 # ---------------------------------------------------------------------------- swa_concat
 
 @pytest.mark.parametrize("dt,D,r", [("fp32", 64, 16), ("bf16", 512, 64), ("bf16", 512, 0)])
