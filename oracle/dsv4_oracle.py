@@ -35,6 +35,11 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
                            heads reach only its rank slice), identity weights.  The grouping
                            of consecutive heads and the linear-layer weight layout are
                            readings (R22); the page prints no values for them.
+  input_projections        pinned: brute-force loops on tiny shapes, one-hot rows pick each
+                           weight's column (which output reads which weight), the merged
+                           query weight (W_qb W_qa) closed form, token locality.  Which
+                           input feeds each projection and the absence of a norm are readings
+                           (R23/R24); the page prints no values for them.
 """
 from __future__ import annotations
 
@@ -462,3 +467,47 @@ def grouped_out_proj(attn, w_a, w_b, groups: int, round_intermediate: bool = Fal
     if round_intermediate:
         mid = round_bf16(mid)
     return mid @ w_b.T, mid
+
+
+# ----------------------------------------------------------------------------
+# input projections of one attention layer
+# ----------------------------------------------------------------------------
+
+# Which projections a layer of each type has, in the order the outputs are listed.  Those of
+# the first group read the hidden state x; those of the second read the query latent c_q.
+INPROJ_FROM_X = {
+    "sliding": ("q_a", "kv"),
+    "hca": ("q_a", "kv", "gate"),
+    "csa": ("q_a", "kv", "gate", "k_idx", "g_idx", "w_idx"),
+}
+INPROJ_FROM_LATENT = {"sliding": ("q",), "hca": ("q",), "csa": ("q", "q_idx")}
+
+
+def input_projections(x, weights, kind: str, round_latent: bool = False):
+    """The projections that produce the attention core's per-token inputs from the layer's
+    hidden state.
+
+    "Hybrid attention (§2.3)" (kv_proj makes the single K=V head; CSA's compressor with its
+    gate and the Lightning Indexer of eqs. 13-17 with index_n_heads query heads of
+    index_head_dim and per-head weights) and "DeepseekV4Config" (q_lora_rank: the query goes
+    through a rank-q_lora_rank factorisation; attention_bias False: no bias anywhere).
+    Readings R23/R24: every projection is a plain linear map with a linear layer's
+    [out, in] weight and nothing between the two query factors (the page names no norm);
+    the query latent c_q = x W_qa^T feeds both the attention query q = c_q W_qb^T and the
+    indexer query q_idx = c_q W_q_idx^T, while kv, the compressor gate, the indexer key
+    content k_idx, its gate g_idx and the indexer head weights w_idx project x directly.
+    ``round_latent`` models bf16 storage of c_q before the second factor.
+
+    x [T, hidden]; ``weights`` maps each name of INPROJ_FROM_X[kind] and
+    INPROJ_FROM_LATENT[kind] to its [width, in] matrix ("q_a" is [q_rank, hidden]).
+    Returns {"c_q": [T, q_rank], name: [T, width] for every other name}.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = {k: np.asarray(v, dtype=np.float64) for k, v in weights.items()}
+    out = {}
+    for name in INPROJ_FROM_X[kind]:
+        out["c_q" if name == "q_a" else name] = x @ W[name].T
+    lat = round_bf16(out["c_q"]) if round_latent else out["c_q"]
+    for name in INPROJ_FROM_LATENT[kind]:
+        out[name] = lat @ W[name].T
+    return out

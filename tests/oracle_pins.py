@@ -514,4 +514,92 @@ def pin_oproj_identity(O):
     _close(mid, attn.reshape(4, K), 0.0, "identity intermediate")
 
 
+# ----------------------------------------------------------------------------
+# input projections (readings R23/R24)
+# ----------------------------------------------------------------------------
+
+_INPROJ_WIDTH = {"q_a": 4, "kv": 3, "gate": 3, "k_idx": 2, "g_idx": 2, "w_idx": 2, "q": 5, "q_idx": 6}
+
+
+def _inproj_case(seed, kind, T=3, hidden=7):
+    """Tiny distinct widths, so a name wired to the wrong weight changes a shape or a value."""
+    r = RNG(seed)
+    x = r.standard_normal((T, hidden))
+    ws = {}
+    for n in _inproj_names(kind):
+        fan_in = _INPROJ_WIDTH["q_a"] if n in ("q", "q_idx") else hidden
+        ws[n] = r.standard_normal((_INPROJ_WIDTH[n], fan_in))
+    return x, ws
+
+
+def _inproj_names(kind):
+    return {"sliding": ("q_a", "kv", "q"), "hca": ("q_a", "kv", "gate", "q"),
+            "csa": ("q_a", "kv", "gate", "k_idx", "g_idx", "w_idx", "q", "q_idx")}[kind]
+
+
+def pin_inproj_bruteforce(O):
+    """Explicit loops over every output element: the latent from x, q and q_idx from the
+    latent, the others from x; each layer type lists exactly its own outputs."""
+    for kind in ("csa", "hca", "sliding"):
+        x, ws = _inproj_case(21, kind)
+        got = O.input_projections(x, ws, kind)
+        T, hidden = x.shape
+        lat = np.zeros((T, _INPROJ_WIDTH["q_a"]))
+        for t in range(T):
+            for j in range(lat.shape[1]):
+                lat[t, j] = sum(x[t, k] * ws["q_a"][j, k] for k in range(hidden))
+        want = {"c_q": lat}
+        for n in _inproj_names(kind):
+            if n == "q_a":
+                continue
+            src = lat if n in ("q", "q_idx") else x
+            y = np.zeros((T, _INPROJ_WIDTH[n]))
+            for t in range(T):
+                for j in range(y.shape[1]):
+                    y[t, j] = sum(src[t, k] * ws[n][j, k] for k in range(src.shape[1]))
+            want[n] = y
+        assert sorted(got) == sorted(want), (kind, sorted(got))
+        for n in want:
+            _close(got[n], want[n], 1e-12, f"{kind} {n}")
+
+
+def pin_inproj_one_hot_rows(O):
+    """Row x = e_j gives column j of every weight read from x, and q / q_idx of the latent
+    W_qa[:, j] (a wrong weight, a transposed one or a wrong input fails here)."""
+    x, ws = _inproj_case(22, "csa", T=1)
+    hidden = x.shape[1]
+    for j in range(hidden):
+        e = np.zeros((1, hidden))
+        e[0, j] = 1.0
+        got = O.input_projections(e, ws, "csa")
+        _close(got["c_q"][0], ws["q_a"][:, j], 0.0, f"c_q e_{j}")
+        for n in ("kv", "gate", "k_idx", "g_idx", "w_idx"):
+            _close(got[n][0], ws[n][:, j], 0.0, f"{n} e_{j}")
+        for n in ("q", "q_idx"):
+            _close(got[n][0], ws[n] @ ws["q_a"][:, j], 1e-12, f"{n} e_{j}")
+
+
+def pin_inproj_merged_query_weight(O):
+    """The two query factors compose to the single product x (W_qb W_qa)^T, and with an
+    identity first factor the query is the one-factor projection of x."""
+    x, ws = _inproj_case(23, "hca", T=4)
+    got = O.input_projections(x, ws, "hca")
+    _close(got["q"], x @ (ws["q"] @ ws["q_a"]).T, 1e-12, "merged query weight")
+    ws2 = dict(ws, q_a=np.eye(x.shape[1]), q=RNG(24).standard_normal((5, x.shape[1])))
+    _close(O.input_projections(x, ws2, "hca")["q"], x @ ws2["q"].T, 1e-12, "identity first factor")
+    _close(O.input_projections(x, ws2, "hca")["c_q"], x, 0.0, "identity latent")
+
+
+def pin_inproj_token_locality(O):
+    """Each output row depends on its own token's hidden state only."""
+    x, ws = _inproj_case(25, "csa", T=5)
+    base = O.input_projections(x, ws, "csa")
+    x2 = x.copy()
+    x2[2] += 1.0
+    moved = O.input_projections(x2, ws, "csa")
+    for n in base:
+        d = np.abs(moved[n] - base[n]).max(axis=1)
+        assert d[2] > 0 and not np.delete(d, 2).any(), n
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -59,6 +59,12 @@ MUTATIONS = {
     "oproj_group_order_reversed": [("mid[:, g * rank:(g + 1) * rank] = a[:, g * kg:(g + 1) * kg] @ w_a[g].T",
                                     "mid[:, g * rank:(g + 1) * rank] = a[:, g * kg:(g + 1) * kg] @ w_a[groups - 1 - g].T")],
     "oproj_second_product_dropped": [("return mid @ w_b.T, mid", "return mid[:, :w_b.shape[0]], mid")],
+    "inproj_gate_reads_kv_weight": [('out["c_q" if name == "q_a" else name] = x @ W[name].T',
+                                     'out["c_q" if name == "q_a" else name] = x @ W["kv" if name == "gate" else name].T')],
+    "inproj_latent_always_rounded": [('lat = round_bf16(out["c_q"]) if round_latent else out["c_q"]',
+                                      'lat = round_bf16(out["c_q"])')],
+    "inproj_indexer_query_from_query": [("out[name] = lat @ W[name].T",
+                                         "out[name] = lat @ W[name].T if name == \"q\" else out[\"q\"][:, :W[name].shape[0]]")],
 }
 
 
