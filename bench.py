@@ -416,6 +416,46 @@ def run_oproj(torch, steps, warmup):
             "frac": flops / ms / 1e9 / (PEAK_BF16 / 1e12), "tokens_per_s": T / ms * 1e3}
 
 
+def run_inproj(torch, steps, warmup):
+    """The input projections of the S=8192 CSA layer: 8192 tokens of hidden 4096 -> the query
+    latent (q_lora_rank 1024), K=V head and compressor gate (512 each), indexer key content and
+    gate (128 each) and head weights (64, fp32); then the latent -> 64 x 512 query heads and
+    64 x 128 indexer query heads (DeepseekV4Config defaults).  Inputs are generated on the
+    device (N(0,1) hidden state, fan-in-scaled N(0,1) weights, bf16)."""
+    import workloads as W
+    from long_context_sparse_09_amd import input_projections
+
+    w = W.workload(2)
+    T, hid, qr = w.S, w.hidden, w.q_rank
+    wd = W.inproj_widths(w)
+    n_x = sum(wd[n] for n in W.INPROJ_X_ORDER["csa"])
+    n_lat = sum(wd[n] for n in W.INPROJ_LAT_ORDER["csa"])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed * 1000 + 91)
+    x = torch.randn((T, hid), generator=g, device="cuda").to(torch.bfloat16)
+    w_x = (torch.randn((n_x, hid), generator=g, device="cuda") / hid ** 0.5).to(torch.bfloat16)
+    w_lat = (torch.randn((n_lat, qr), generator=g, device="cuda") / qr ** 0.5).to(torch.bfloat16)
+    e = lambda *sh, dt=torch.bfloat16: torch.empty(*sh, dtype=dt, device="cuda")  # noqa: E731
+    out = dict(c_q=e(T, qr), q=e(T, w.H, w.D), kv=e(T, w.D), gate=e(T, w.D), q_idx=e(T, w.nI, w.cI),
+               k_idx=e(T, w.cI), g_idx=e(T, w.cI), w_idx=e(T, w.nI, dt=torch.float32))
+    for _ in range(warmup):
+        input_projections("csa", x, w_x, w_lat, **out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        input_projections("csa", x, w_x, w_lat, **out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * T * (n_x * hid + n_lat * qr)
+    return {"workload": f"input_projections T=8192 CSA: 4096 -> {n_x} (latent, kv, gate, indexer k/g/w); "
+                        f"1024 -> {n_lat} (q, indexer q) (bf16)", "ms": ms,
+            "alg_flops": flops, "TFLOP/s": flops / ms / 1e9, "bound": "mfma",
+            "frac": flops / ms / 1e9 / (PEAK_BF16 / 1e12), "tokens_per_s": T / ms * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,7 +463,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the HCA / decode workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["csa_prefill", "hca_prefill", "csa_decode", "stack", "oproj"], default=None,
+    ap.add_argument("--only", choices=["csa_prefill", "hca_prefill", "csa_decode", "stack", "oproj", "inproj"],
+                    default=None,
                     help="run one workload alone (for profiling); prints its figures only")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="launch one device copy of this size first (counter calibration)")
@@ -444,9 +485,9 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written")
         del src, dst
-    if args.only in ("hca_prefill", "csa_decode", "stack", "oproj"):
+    if args.only in ("hca_prefill", "csa_decode", "stack", "oproj", "inproj"):
         fn = {"hca_prefill": run_hca_prefill, "csa_decode": run_decode,
-              "stack": run_stack, "oproj": run_oproj}[args.only]
+              "stack": run_stack, "oproj": run_oproj, "inproj": run_inproj}[args.only]
         print(json.dumps({"only": args.only, **fn(torch, args.steps, args.warmup)}), flush=True)
         return
     w, wall, kern = run_csa_prefill(torch, args.steps, args.warmup)
@@ -463,6 +504,7 @@ def main():
         extra["stack8_prefill"] = run_stack(torch, max(2, args.steps // 5), 1)
         torch.cuda.empty_cache()
         extra["grouped_out_proj"] = run_oproj(torch, args.steps, args.warmup)
+        extra["input_projections"] = run_inproj(torch, args.steps, args.warmup)
         torch.cuda.empty_cache()
     att = kern["csa_attend"]
     src = kernel_hash("attend_mfma.hip", "common.h")

@@ -247,7 +247,7 @@ int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
  *   mid  : caller-owned [T, groups * rank] dtype buffer for the intermediate (written).
  *   out  : [T, hidden] dtype.  Accumulation is fp32; mid is stored in dtype.
  *   groups must divide H.  Every [T, .] operand below 2 GiB (DSV4_ERR_UNSUPPORTED beyond).
- *   bf16 with rank and hidden multiples of 256 and H/groups * D, groups * rank multiples of 64
+ *   bf16 with rank and hidden multiples of 32 and H/groups * D, groups * rank multiples of 64
  *   runs on the MFMA path; other shapes run a plain kernel (same results up to rounding order).
  */
 int grouped_out_proj(const void* attn, const void* w_a, const void* w_b, void* mid, void* out, int T,
@@ -259,9 +259,48 @@ int grouped_out_proj(const void* attn, const void* w_a, const void* w_b, void* m
  * indexer and the attention are products of the same form).
  *
  *   x : [M, K] dtype.  w : [N, K] dtype (a linear layer's [out, in] weight).  y : [M, N] dtype.
- *   fp32 accumulation.  bf16 with N % 256 == 0 and K % 64 == 0 runs on the MFMA path.
+ *   fp32 accumulation.  bf16 with N % 32 == 0 and K % 64 == 0 runs on the MFMA path.
  */
 int linear_bt(const void* x, const void* w, void* y, int M, int N, int K, int dtype, void* stream);
+
+/*
+ * linear_bt_multi - several linear maps of one input in one product: the weights stacked
+ * row-wise in w, each map's result written to its own buffer (the projections that read the
+ * same input, "Hybrid attention (§2.3)": kv_proj, the compressor gate, the indexer's key
+ * content, gate and head weights, the query's first factor).
+ *
+ *   x : [M, K] dtype.  w : [sum(widths), K] dtype, map s in rows sum(widths[0..s-1]) onward.
+ *   outs[s] : [M, widths[s]] row-major, fp32 when out_f32[s] = 1 else dtype (bf16 inputs may
+ *   give fp32 outputs; fp32 inputs give fp32 only).  1 <= n_out <= 8.  fp32 accumulation.
+ *   Outputs are overwritten; no buffer may overlap another or x.  bf16 with K % 64 == 0 and
+ *   every width a multiple of 32 runs on the MFMA path, other shapes on a plain kernel.
+ *   Errors: DSV4_ERR_INVALID for a bad count, width, flag or pointer.
+ */
+int linear_bt_multi(const void* x, const void* w, int M, int K, int n_out, void* const* outs,
+                    const int* widths, const int* out_f32, int dtype, void* stream);
+
+/*
+ * input_projections - the projections that make one attention layer's per-token inputs from
+ * its hidden state ("Hybrid attention (§2.3)": kv_proj's single K=V head, CSA's compressor
+ * gate and the Lightning Indexer of eqs. 13-17; "DeepseekV4Config": q_lora_rank,
+ * index_n_heads, index_head_dim; attention_bias False).  Reading: plain linear maps, no bias,
+ * no norm between the query factors; the query latent c_q = x . W_qa^T feeds the attention
+ * query q and the indexer query q_idx, every other output reads x.
+ *
+ *   kind  : 0 sliding (c_q, q, kv), 2 HCA (adds gate), 1 CSA (adds gate, q_idx, k_idx, g_idx,
+ *           w_idx).  Outputs a layer type does not have are ignored (may be NULL).
+ *   x     : [T, hidden] dtype.
+ *   w_x   : rows [W_qa (q_rank) | W_kv (D) | W_gate (D) | W_kI (cI) | W_gI (cI) | W_wI (nI)]
+ *           of length hidden, the layer's subset in this order, dtype.
+ *   w_lat : rows [W_qb (H * D) | W_qI (nI * cI)] of length q_rank (W_qI for CSA only), dtype.
+ *   c_q [T, q_rank], q [T, H, D], kv, gate [T, D], q_idx [T, nI, cI], k_idx, g_idx [T, cI]:
+ *           dtype (c_q is written first and read back, so it is stored in dtype).
+ *   w_idx [T, nI] fp32.  Two launches on `stream`; fp32 accumulation.
+ *   Errors: DSV4_ERR_INVALID for a bad kind, size or missing output.
+ */
+int input_projections(int kind, const void* x, const void* w_x, const void* w_lat, void* c_q, void* q,
+                      void* kv, void* gate, void* q_idx, void* k_idx, void* g_idx, float* w_idx, int T,
+                      int hidden, int q_rank, int H, int D, int nI, int cI, int dtype, void* stream);
 
 /*
  * attention_mask_dump - render one layer's attention visibility for auditing ("Attention mask

@@ -7,13 +7,14 @@ PyTorch supplies device memory and the current stream only.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 from . import _lib
 
 __all__ = ["csa_compress", "compressor_cache_update", "csa_index_topk",
            "csa_index_topk_workspace_size", "swa_concat", "csa_attend", "hca_attend",
-           "attend_workspace_size", "grouped_out_proj", "linear_bt", "attention_mask_dump",
+           "attend_workspace_size", "grouped_out_proj", "linear_bt", "linear_bt_multi", "input_projections", "attention_mask_dump",
            "abi_version", "DSV4Error", "lib"]
 
 DSV4_FP32, DSV4_BF16 = 0, 1
@@ -210,6 +211,54 @@ def linear_bt(x, w, y, stream=None) -> None:
     _check("linear_bt", lib().linear_bt(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dtype(x), _stream(stream)))
 
 
+def linear_bt_multi(x, w, outs, stream=None) -> None:
+    """outs[s] [M, width_s] = x [M,K] . (rows of w [sum width, K] for map s)^T; bf16 inputs may
+    write fp32 outputs."""
+    import torch
+
+    M, K = x.shape
+    if w.shape[1] != K or w.shape[0] != sum(o.shape[1] for o in outs):
+        raise ValueError(f"w {tuple(w.shape)} does not stack the outputs' widths over K={K}")
+    if any(o.dim() != 2 or o.shape[0] != M for o in outs):
+        raise ValueError("every output must be [M, width]")
+    n = len(outs)
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(o) for o in outs])
+    widths = (ctypes.c_int * n)(*[o.shape[1] for o in outs])
+    f32 = (ctypes.c_int * n)(*[int(o.dtype == torch.float32) for o in outs])
+    _check("linear_bt_multi", lib().linear_bt_multi(_ptr(x), _ptr(w), M, K, n, ptrs, widths, f32,
+                                                    _dtype(x), _stream(stream)))
+
+
+def input_projections(kind: str, x, w_x, w_lat, c_q, q, kv, gate=None, q_idx=None, k_idx=None,
+                      g_idx=None, w_idx=None, stream=None) -> None:
+    """x [T,hidden]; w_x [q_rank + D (+ D) (+ 2 cI + nI), hidden]; w_lat [H*D (+ nI*cI), q_rank];
+    c_q [T,q_rank]; q [T,H,D]; kv, gate [T,D]; q_idx [T,nI,cI]; k_idx, g_idx [T,cI]; w_idx [T,nI]
+    fp32.  kind "sliding" / "hca" / "csa" (outputs the type lacks stay None)."""
+    T, hidden = x.shape
+    q_rank = c_q.shape[1]
+    _, H, D = q.shape
+    k = _MASK_KINDS[kind]
+    nI, cI = (q_idx.shape[1], q_idx.shape[2]) if k == 1 else (0, 0)
+    n_x = q_rank + D + (D if k else 0) + (2 * cI + nI if k == 1 else 0)
+    n_lat = H * D + nI * cI
+    if tuple(w_x.shape) != (n_x, hidden) or tuple(w_lat.shape) != (n_lat, q_rank):
+        raise ValueError(f"w_x {tuple(w_x.shape)} / w_lat {tuple(w_lat.shape)}: expected "
+                         f"{(n_x, hidden)} / {(n_lat, q_rank)}")
+    want = {"c_q": (c_q, (T, q_rank)), "q": (q, (T, H, D)), "kv": (kv, (T, D))}
+    if k:
+        want["gate"] = (gate, (T, D))
+    if k == 1:
+        want.update(q_idx=(q_idx, (T, nI, cI)), k_idx=(k_idx, (T, cI)), g_idx=(g_idx, (T, cI)),
+                    w_idx=(w_idx, (T, nI)))
+    for name, (t, shape) in want.items():
+        if t is None or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be a tensor of shape {shape}")
+    _check("input_projections", lib().input_projections(
+        k, _ptr(x), _ptr(w_x), _ptr(w_lat), _ptr(c_q), _ptr(q), _ptr(kv), _ptr(gate), _ptr(q_idx),
+        _ptr(k_idx), _ptr(g_idx), _ptr(w_idx), T, hidden, q_rank, H, D, nI, cI, _dtype(x),
+        _stream(stream)))
+
+
 _MASK_KINDS = {"sliding": 0, "csa": 1, "hca": 2}
 _MASK_FORMATS = {"text": 0, "ansi": 1, "svg": 2, "lists": 3}
 
@@ -218,8 +267,6 @@ def attention_mask_dump(kind: str, S: int, window: int, m: int = 1, topk_idx=Non
                         n_entries: int = 0, q_pos0: int = 0, fmt: str = "text") -> str:
     """Visibility grid / SVG / index-list dump of one layer (host only).  topk_idx: [S, k]
     int32 lists (numpy array or tensor; copied to host memory) for kind "csa"."""
-    import ctypes
-
     import numpy as np
 
     ptr, k, keep = None, 0, None

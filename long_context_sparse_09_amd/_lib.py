@@ -26,6 +26,11 @@ SIGNATURES = {
     "grouped_out_proj": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                           c_int, c_int, c_int, c_int, c_void_p], c_int),
     "linear_bt": ([c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p], c_int),
+    "linear_bt_multi": ([c_void_p, c_void_p, c_int, c_int, c_int, ctypes.POINTER(c_void_p),
+                         ctypes.POINTER(c_int), ctypes.POINTER(c_int), c_int, c_void_p], c_int),
+    "input_projections": ([c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                           c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                           c_int, c_int, c_int, c_void_p], c_int),
     "attention_mask_dump": ([c_int, c_int, c_int, c_int, c_void_p, c_int, c_int, c_ll, c_int,
                              c_char_p, c_size_t, ctypes.POINTER(c_size_t)], c_int),
     "csa_compress_split": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,

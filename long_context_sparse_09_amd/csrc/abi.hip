@@ -200,6 +200,64 @@ int grouped_out_proj(const void* attn, const void* w_a, const void* w_b, void* m
                   "grouped_out_proj (o_b)");
 }
 
+int linear_bt_multi(const void* x, const void* w, int M, int K, int n_out, void* const* outs, const int* widths,
+                    const int* out_f32, int dtype, void* stream) {
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(M >= 0 && K >= 1, "M >= 0 and K >= 1 required");
+  REQUIRE(n_out >= 1 && n_out <= dsv4::kGemmMaxSeg, "n_out %d outside [1, %d]", n_out, dsv4::kGemmMaxSeg);
+  REQUIRE(outs && widths && out_f32, "null outs/widths/out_f32");
+  dsv4::GemmOut o{};
+  o.n_seg = n_out;
+  long long N = 0;
+  for (int s = 0; s < n_out; ++s) {
+    REQUIRE(widths[s] >= 1, "widths[%d] = %d must be >= 1", s, widths[s]);
+    REQUIRE(out_f32[s] == 0 || out_f32[s] == 1, "out_f32[%d] must be 0 or 1", s);
+    REQUIRE(dtype == DSV4_BF16 || out_f32[s] == 1, "fp32 inputs give fp32 outputs only");
+    o.begin[s] = static_cast<int>(N);
+    N += widths[s];
+    o.f32[s] = out_f32[s];
+    o.ld[s] = widths[s];
+    o.ptr[s] = outs[s];
+  }
+  REQUIRE(N < (1LL << 30), "total width %lld too large", N);
+  o.begin[n_out] = static_cast<int>(N);
+  if (M == 0) return ok();
+  REQUIRE(x && w, "null x/w");
+  REQUIRE(aligned16(x) && aligned16(w), "pointers must be 16-byte aligned");
+  for (int s = 0; s < n_out; ++s) REQUIRE(outs[s] && aligned16(outs[s]), "outs[%d] null or not 16-byte aligned", s);
+  return launched(dsv4::launch_gemm_bt_seg(x, w, o, M, K, K, K, 1, 0, 0, dtype, static_cast<hipStream_t>(stream)),
+                  "linear_bt_multi");
+}
+
+int input_projections(int kind, const void* x, const void* w_x, const void* w_lat, void* c_q, void* q, void* kv,
+                      void* gate, void* q_idx, void* k_idx, void* g_idx, float* w_idx, int T, int hidden,
+                      int q_rank, int H, int D, int nI, int cI, int dtype, void* stream) {
+  REQUIRE(kind >= 0 && kind <= 2, "kind %d: 0 sliding, 1 CSA, 2 HCA", kind);
+  REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
+  REQUIRE(T >= 0 && hidden >= 1 && q_rank >= 1 && H >= 1 && D >= 1, "sizes must be positive");
+  REQUIRE(kind != 1 || (nI >= 1 && cI >= 1), "CSA needs nI, cI >= 1");
+  REQUIRE(static_cast<long long>(H) * D < (1LL << 28) && static_cast<long long>(nI) * cI < (1LL << 28),
+          "query width too large");
+  // stage 1 reads x: [c_q | kv | gate | k_idx | g_idx | w_idx] (the layer's subset, in this order)
+  void* o1[6] = {c_q, kv, gate, k_idx, g_idx, w_idx};
+  const int wd1[6] = {q_rank, D, D, cI, cI, nI};
+  const int f1[6] = {dtype == DSV4_FP32, dtype == DSV4_FP32, dtype == DSV4_FP32, dtype == DSV4_FP32,
+                     dtype == DSV4_FP32, 1};
+  const int n1 = kind == 0 ? 2 : kind == 2 ? 3 : 6;
+  // stage 2 reads c_q: [q | q_idx]
+  void* o2[2] = {q, q_idx};
+  const int wd2[2] = {H * D, kind == 1 ? nI * cI : 0};
+  const int f2[2] = {dtype == DSV4_FP32, dtype == DSV4_FP32};
+  const int n2 = kind == 1 ? 2 : 1;
+  if (T == 0) return ok();
+  REQUIRE(x && w_x && w_lat, "null x/w_x/w_lat");
+  for (int s = 0; s < n1; ++s) REQUIRE(o1[s], "null output %d of the hidden-state projections", s);
+  for (int s = 0; s < n2; ++s) REQUIRE(o2[s], "null output %d of the latent projections", s);
+  int rc = linear_bt_multi(x, w_x, T, hidden, n1, o1, wd1, f1, dtype, stream);
+  if (rc != DSV4_OK) return rc;
+  return linear_bt_multi(c_q, w_lat, T, q_rank, n2, o2, wd2, f2, dtype, stream);
+}
+
 int attention_mask_dump(int kind, int S, int window, int m, const int* topk_idx, int k,
                         int n_entries, long long q_pos0, int format, char* buf, size_t buf_bytes,
                         size_t* needed) {

@@ -7,11 +7,17 @@
 // hidden_size).  Both factors are dense contractions: the grouped one is a batch of o_groups
 // independent products (one per head group), the second a single product.
 //
-// Operands: A [M, K] rows of stride lda, B [N, K] rows of stride ldb (a linear layer's
-// [out, in] weight), C [M, N] rows of stride ldc; batch g offsets all three by sA, sB, sC.
-// Both factors are K-contiguous, so their tiles move and are read the same way.
+// The layer's input projections are the same kind of product: several linear maps of one
+// input, whose weights stacked row-wise make one B, so one launch fills the chip where the
+// narrow ones alone (64 or 128 columns) would not.  The columns of C then split into
+// segments, each stored in its own buffer and type (the indexer head weights in fp32).
 //
-// bf16 path (N % 256 == 0, K % 64 == 0):
+// Operands: A [M, K] rows of stride lda, B [N, K] rows of stride ldb (a linear layer's
+// [out, in] weight), C's column segments as described by GemmOut; batch g offsets A, B and
+// each segment by sA, sB and the segment's stride.  Both factors are K-contiguous, so their
+// tiles move and are read the same way.
+//
+// bf16 path (K % 64 == 0, every output segment a multiple of 32 columns wide):
 //   * one 256 x 256 tile of C per workgroup, four waves of 128 x 128 (one per SIMD), 64-deep
 //     K steps on v_mfma_f32_32x32x16_bf16; the accumulators (256 per lane) sit in the
 //     accumulator registers;
@@ -24,7 +30,8 @@
 //     side), so the 32-row fragment reads are conflict-free;
 //   * the wave computes C^T blocks (A's fragment as the B operand), so that each lane holds
 //     4 consecutive output columns per group and a 32-lane swap makes 16-byte stores;
-//   * rows at or beyond M read zeros and their stores fall outside the buffer descriptor.
+//   * rows at or beyond M (and B rows at or beyond N in a ragged last tile column) read
+//     zeros; their stores are skipped.
 #include "common.h"
 #include "launch.h"
 
@@ -32,6 +39,7 @@ namespace dsv4 {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 gbf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float gf32x16_t;
+typedef __attribute__((ext_vector_type(4))) float gf32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned gu32x4_t;
 
 namespace {
@@ -59,9 +67,8 @@ __device__ __forceinline__ int gswz(int row) { return (row >> 1) & 7; }
 }  // namespace
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_bt_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C, int M, int N,
-             int K, long long lda, long long ldb, long long ldc, long long sA, long long sB, long long sC,
-             int tiles_n) {
+gemm_bt_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const GemmOut out, int M, int N, int K,
+             long long lda, long long ldb, long long sA, long long sB, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) unsigned char glds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -73,7 +80,9 @@ gemm_bt_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
   const bf16_t* Bb = B + g * sB;
   const grsrc_t a_rs = gmake_rs(Ab + static_cast<long long>(m0) * lda,
                                 static_cast<unsigned long long>(M - m0) * lda * 2);
-  const grsrc_t b_rs = gmake_rs(Bb + static_cast<long long>(n0) * ldb, static_cast<unsigned long long>(GN) * ldb * 2);
+  // B covers rows n0 .. N-1 of this tile column only (a ragged last column reads zeros)
+  const grsrc_t b_rs = gmake_rs(Bb + static_cast<long long>(n0) * ldb,
+                                static_cast<unsigned long long>(N - n0 < GN ? N - n0 : GN) * ldb * 2);
   // Load lanes: per K step each operand tile is 32 loads of 1 KB (8 rows x 128 bytes); wave w
   // issues loads 8w .. 8w + 7 of each.  Lane l fills LDS chunk l % 8 of row 8 i + l / 8 with
   // the global chunk (l % 8) ^ swz(row).
@@ -148,14 +157,42 @@ gemm_bt_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
   }
 
   // epilogue: C^T block (ni, mi) holds, for output row m = m0 + 128 wm + 32 mi + l32, columns
-  // n0 + 128 wn + 32 ni + 8 q + 4 half + 0..3 (q = 0..3); a 32-lane swap gives each lane 8.
-  const grsrc_t c_rs = gmake_rs(C + g * sC, static_cast<unsigned long long>(M) * ldc * 2);
+  // nb + 8 q + 4 half + 0..3 (q = 0..3), nb = n0 + 128 wn + 32 ni.  Segment bounds are
+  // multiples of 32, so a block lies in one output segment, looked up once per block.  bf16:
+  // a 32-lane swap gives each lane 8 consecutive columns (one 16-byte store per 16 columns);
+  // fp32: each lane stores its own 4-column runs.
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const long long m = m0 + 128 * wm + 32 * mi + l32;
-    const unsigned row_off = static_cast<unsigned>(m < M ? m * ldc * 2 : 0xFFFFFFF0ull);
+  for (int ni = 0; ni < 4; ++ni) {
+    const int nb = n0 + 128 * wn + 32 * ni;
+    if (nb >= N) break;
+    int s = 0;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int i = 1; i < kGemmMaxSeg; ++i) s += (i < out.n_seg && nb >= out.begin[i]) ? 1 : 0;
+    s = __builtin_amdgcn_readfirstlane(s);
+    const int col = nb - out.begin[s];
+    const bool f32 = out.f32[s] != 0;
+    const long long ld = out.ld[s];
+    const int esz = f32 ? 4 : 2;
+    const unsigned char* cbase = static_cast<const unsigned char*>(out.ptr[s]) +
+                                 (g * out.stride[s] + static_cast<long long>(m0) * ld) * esz;
+    const grsrc_t c_rs = gmake_rs(cbase, static_cast<unsigned long long>(M - m0) * ld * esz);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int ml = 128 * wm + 32 * mi + l32;  // row within the tile
+      const bool live = m0 + ml < M;
+      const unsigned row_off = static_cast<unsigned>(static_cast<long long>(ml) * ld * esz);
+      if (f32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const gf32x4_t v4 = {acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1], acc[ni][mi][4 * q + 2],
+                               acc[ni][mi][4 * q + 3]};
+          const gu32x4_t val = __builtin_bit_cast(gu32x4_t, v4);
+          if (live)
+            __builtin_amdgcn_raw_buffer_store_b128(val, c_rs, row_off + static_cast<unsigned>(col + 8 * q + 4 * half) * 4,
+                                                   0, 0);
+        }
+        continue;
+      }
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
         unsigned w[2][2];
@@ -173,9 +210,9 @@ gemm_bt_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
         val[2] = s0[1];
         val[3] = s1[1];
         // lanes < 32 write columns 16 gp + 0..7 of the block, lanes >= 32 columns 16 gp + 8..15
-        const int n = n0 + 128 * wn + 32 * ni + 16 * gp + 8 * half;
-        if (row_off != 0xFFFFFFF0u)
-          __builtin_amdgcn_raw_buffer_store_b128(val, c_rs, row_off + static_cast<unsigned>(n) * 2, 0, 0);
+        if (live)
+          __builtin_amdgcn_raw_buffer_store_b128(val, c_rs, row_off + static_cast<unsigned>(col + 16 * gp + 8 * half) * 2,
+                                                 0, 0);
       }
     }
   }
@@ -184,9 +221,8 @@ gemm_bt_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
 // Any shape, bf16 or fp32 storage, fp32 accumulation: one thread per output element.
 template <typename T>
 __global__ void __launch_bounds__(256) gemm_bt_generic(const T* __restrict__ A, const T* __restrict__ B,
-                                                       T* __restrict__ C, int M, int N, int K, long long lda,
-                                                       long long ldb, long long ldc, long long sA, long long sB,
-                                                       long long sC) {
+                                                       const GemmOut out, int M, int N, int K, long long lda,
+                                                       long long ldb, long long sA, long long sB) {
   const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
   const int g = blockIdx.y;
   if (idx >= static_cast<long long>(M) * N) return;
@@ -205,20 +241,30 @@ __global__ void __launch_bounds__(256) gemm_bt_generic(const T* __restrict__ A, 
     }
     acc = fmaf(x, y, acc);
   }
-  T* c = C + g * sC + m * ldc + n;
-  if constexpr (sizeof(T) == 2) *c = f32_to_bf16(acc);
-  else *c = acc;
+  int s = 0;
+  for (int i = 1; i < out.n_seg; ++i) s += n >= out.begin[i] ? 1 : 0;
+  const long long off = g * out.stride[s] + m * out.ld[s] + (n - out.begin[s]);
+  if (out.f32[s]) static_cast<float*>(out.ptr[s])[off] = acc;
+  else static_cast<bf16_t*>(out.ptr[s])[off] = f32_to_bf16(acc);
 }
 
-bool gemm_fast(int N, int K, long long lda, long long ldb, long long ldc, int dtype) {
-  return dtype == 1 && N % GN == 0 && K % GK == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldc % 8 == 0;  // 16-byte rows
+bool gemm_fast(const GemmOut& out, int K, long long lda, long long ldb, int dtype) {
+  // 16-byte operand rows and in-tile byte offsets that fit 32 bits
+  if (dtype != 1 || K % GK != 0 || lda % 8 != 0 || ldb % 8 != 0 || lda > (1 << 22) || ldb > (1 << 22)) return false;
+  for (int s = 0; s < out.n_seg; ++s) {
+    const int per16 = out.f32[s] ? 4 : 8;  // elements per 16 bytes
+    if ((out.begin[s + 1] - out.begin[s]) % 32 != 0 || out.ld[s] % per16 != 0 || out.stride[s] % per16 != 0 ||
+        out.ld[s] > (1 << 21))
+      return false;
+  }
+  return true;
 }
 
-hipError_t launch_gemm_bt(const void* A, const void* B, void* C, int M, int N, int K, long long lda,
-                          long long ldb, long long ldc, int batch, long long sA, long long sB, long long sC,
-                          int dtype, hipStream_t st) {
+hipError_t launch_gemm_bt_seg(const void* A, const void* B, const GemmOut& out, int M, int K, long long lda,
+                              long long ldb, int batch, long long sA, long long sB, int dtype, hipStream_t st) {
+  const int N = out.begin[out.n_seg];
   if (M == 0 || N == 0 || batch == 0) return hipSuccess;
-  if (gemm_fast(N, K, lda, ldb, ldc, dtype)) {
+  if (gemm_fast(out, K, lda, ldb, dtype)) {
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bt_mfma),
@@ -226,21 +272,35 @@ hipError_t launch_gemm_bt(const void* A, const void* B, void* C, int M, int N, i
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    const int tiles_m = (M + GM - 1) / GM, tiles_n = N / GN;
+    const int tiles_m = (M + GM - 1) / GM, tiles_n = (N + GN - 1) / GN;
     hipLaunchKernelGGL(gemm_bt_mfma, dim3(tiles_m * tiles_n, batch), dim3(256), kGemmLds, st,
-                       static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), static_cast<bf16_t*>(C), M, N,
-                       K, lda, ldb, ldc, sA, sB, sC, tiles_n);
+                       static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), out, M, N, K, lda, ldb, sA, sB,
+                       tiles_n);
     return hipGetLastError();
   }
   const long long total = static_cast<long long>(M) * N;
   const dim3 grid(static_cast<unsigned>((total + 255) / 256), batch);
   if (dtype == 1)
     hipLaunchKernelGGL(gemm_bt_generic<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(A),
-                       static_cast<const bf16_t*>(B), static_cast<bf16_t*>(C), M, N, K, lda, ldb, ldc, sA, sB, sC);
+                       static_cast<const bf16_t*>(B), out, M, N, K, lda, ldb, sA, sB);
   else
     hipLaunchKernelGGL(gemm_bt_generic<float>, grid, dim3(256), 0, st, static_cast<const float*>(A),
-                       static_cast<const float*>(B), static_cast<float*>(C), M, N, K, lda, ldb, ldc, sA, sB, sC);
+                       static_cast<const float*>(B), out, M, N, K, lda, ldb, sA, sB);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_bt(const void* A, const void* B, void* C, int M, int N, int K, long long lda,
+                          long long ldb, long long ldc, int batch, long long sA, long long sB, long long sC,
+                          int dtype, hipStream_t st) {
+  GemmOut out{};
+  out.n_seg = 1;
+  out.begin[0] = 0;
+  out.begin[1] = N;
+  out.f32[0] = dtype == 0;
+  out.ld[0] = ldc;
+  out.stride[0] = sC;
+  out.ptr[0] = C;
+  return launch_gemm_bt_seg(A, B, out, M, K, lda, ldb, batch, sA, sB, dtype, st);
 }
 
 }  // namespace dsv4

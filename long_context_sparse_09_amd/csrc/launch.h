@@ -91,7 +91,23 @@ int attend_generic_max_keys();
 hipError_t launch_gemm_bt(const void* A, const void* B, void* C, int M, int N, int K, long long lda,
                           long long ldb, long long ldc, int batch, long long sA, long long sB, long long sC,
                           int dtype, hipStream_t st);
-bool gemm_fast(int N, int K, long long lda, long long ldb, long long ldc, int dtype);
+
+// The columns of C split into consecutive segments, each stored in its own buffer: segment s
+// holds columns begin[s] .. begin[s+1]-1 as a row-major [M, begin[s+1]-begin[s]] array with
+// rows of stride ld[s] elements, batch entry g at ptr[s] + g * stride[s] elements, in fp32
+// (f32[s] = 1) or bf16 (0).  begin[0] = 0 and begin[n_seg] = N.
+constexpr int kGemmMaxSeg = 8;
+struct GemmOut {
+  int n_seg;
+  int begin[kGemmMaxSeg + 1];
+  int f32[kGemmMaxSeg];
+  long long ld[kGemmMaxSeg];
+  long long stride[kGemmMaxSeg];
+  void* ptr[kGemmMaxSeg];
+};
+hipError_t launch_gemm_bt_seg(const void* A, const void* B, const GemmOut& out, int M, int K, long long lda,
+                              long long ldb, int batch, long long sA, long long sB, int dtype, hipStream_t st);
+bool gemm_fast(const GemmOut& out, int K, long long lda, long long ldb, int dtype);
 
 // Visibility rendering of one layer (host only).  kind 0 sliding, 1 CSA, 2 HCA; format 0 text,
 // 1 ANSI text, 2 SVG, 3 per-query index lists.  topk_idx: host [S][k] (CSA).

@@ -11,7 +11,7 @@ import pytest
 from long_context_sparse_09_amd import _lib
 
 OK, INVALID, UNSUPPORTED, LAUNCH, WORKSPACE = 0, 1, 2, 3, 4
-BF16 = 1
+FP32, BF16 = 0, 1
 
 
 @pytest.fixture(scope="module")
@@ -183,3 +183,32 @@ def test_split_compressor_argument_errors(lib):
                                              None, None, 2, 512, 4, 64, 64, 1e4, 0, 1, BF16,
                                              None) == INVALID
     assert b"second-projection" in lib.dsv4_last_error()
+
+
+def test_input_projection_argument_errors(lib):
+    P = ctypes.c_void_p
+
+    def multi(M=4, K=64, widths=(32, 64), f32=(0, 1), dtype=BF16, outs=None, xw=None):
+        n = len(widths)
+        o = (P * n)(*(outs if outs is not None else [None] * n))
+        return lib.linear_bt_multi(xw, xw, M, K, n, o, (ctypes.c_int * n)(*widths),
+                                   (ctypes.c_int * n)(*f32), dtype, None)
+    assert multi(widths=(), f32=()) == INVALID                  # no outputs
+    assert multi(widths=(32,) * 9, f32=(0,) * 9) == INVALID     # above the 8-output limit
+    assert multi(widths=(32, 0)) == INVALID and b"widths" in lib.dsv4_last_error()
+    assert multi(f32=(0, 2)) == INVALID
+    assert multi(dtype=FP32, f32=(0, 1)) == INVALID and b"fp32 inputs" in lib.dsv4_last_error()
+    assert multi(M=0) == OK
+    assert multi() == INVALID and b"null" in lib.dsv4_last_error()
+    one = ctypes.c_void_p(64)  # never dereferenced: validation fails first
+    assert multi(outs=[one, None], xw=one) == INVALID and b"outs[1]" in lib.dsv4_last_error()
+
+    def proj(kind=1, T=4, hidden=4096, q_rank=1024, H=64, D=512, nI=64, cI=128, dtype=BF16):
+        return lib.input_projections(kind, None, None, None, None, None, None, None, None, None, None,
+                                     None, T, hidden, q_rank, H, D, nI, cI, dtype, None)
+    assert proj(kind=3) == INVALID and b"kind" in lib.dsv4_last_error()
+    assert proj(q_rank=0) == INVALID
+    assert proj(nI=0) == INVALID and b"CSA" in lib.dsv4_last_error()
+    assert proj(kind=2, nI=0, cI=0, T=0) == OK                # HCA needs no indexer sizes
+    assert proj(T=0) == OK
+    assert proj() == INVALID and b"null" in lib.dsv4_last_error()

@@ -107,11 +107,12 @@ class Workload:
     o_groups: int = 8  # grouped output projection: head groups
     o_rank: int = 1024  # o_lora_rank
     hidden: int = 4096  # hidden_size
+    q_rank: int = 1024  # q_lora_rank
 
 
 WORKLOADS: Dict[int, Workload] = {
     1: Workload(1, "tiny_csa_fp32_S256", "fp32", 1, 256, 8, 64, 16, 4, 128, 4, 32, 16, 32,
-                10000.0, 0, "csa", o_groups=4, o_rank=32, hidden=64),
+                10000.0, 0, "csa", o_groups=4, o_rank=32, hidden=64, q_rank=32),
     2: Workload(2, "csa_prefill_bf16_S8192", "bf16", 1, 8192, 64, 512, 64, 4, 128, 64, 128, 512,
                 128, 10000.0, 2, "csa"),
     3: Workload(3, "hca_prefill_bf16_S65536", "bf16", 1, 65536, 64, 512, 64, 4, 128, 64, 128,
@@ -364,3 +365,35 @@ def oproj_inputs(w: Workload, T: Optional[int] = None, rows=None, layer: int = 0
     return {"attn": encode(attn, w.dtype),
             "w_a": encode(wa.astype(np.float32).reshape(w.o_groups, w.o_rank, kg), w.dtype),
             "w_b": encode(wb.astype(np.float32), w.dtype)}
+
+
+# Projections of one attention layer, by the input they read, in the order the library stacks
+# their weights (rows of w_x, then rows of w_lat).
+INPROJ_X_ORDER = {"sliding": ("q_a", "kv"), "hca": ("q_a", "kv", "gate"),
+                  "csa": ("q_a", "kv", "gate", "k_idx", "g_idx", "w_idx")}
+INPROJ_LAT_ORDER = {"sliding": ("q",), "hca": ("q",), "csa": ("q", "q_idx")}
+
+
+def inproj_widths(w: Workload) -> Dict[str, int]:
+    return {"q_a": w.q_rank, "kv": w.D, "gate": w.D, "k_idx": w.cI, "g_idx": w.cI, "w_idx": w.nI,
+            "q": w.H * w.D, "q_idx": w.nI * w.cI}
+
+
+def inproj_inputs(w: Workload, kind: str, T: Optional[int] = None, rows=None,
+                  layer: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of a layer's input projections: ``x`` [T, hidden] ~ N(0, 1) standing for the
+    layer's hidden state, and one [width, in] weight per projection ~ N(0, 1/in) (fan-in
+    scaling; no trained weights exist here), ``in`` = hidden for those reading x and q_rank for
+    those reading the query latent.  Also ``w_x`` / ``w_lat``: the same weights stacked
+    row-wise in the library's order.  Storage-encoded in the workload's dtype."""
+    T = w.S * w.B if T is None else T
+    rsel = slice(0, T) if rows is None else rows
+    wd = inproj_widths(w)
+    out = {"x": encode(normal_rows(w.seed, layer, "inproj_x", (w.hidden,), rsel, T), w.dtype)}
+    for name in INPROJ_X_ORDER[kind] + INPROJ_LAT_ORDER[kind]:
+        fan_in = w.q_rank if name in INPROJ_LAT_ORDER["csa"] else w.hidden
+        wt = normal_tensor(w.seed, layer, "W_in_" + name, (wd[name], fan_in)) / np.sqrt(fan_in)
+        out[name] = encode(wt.astype(np.float32), w.dtype)
+    out["w_x"] = np.ascontiguousarray(np.concatenate([out[n] for n in INPROJ_X_ORDER[kind]], axis=0))
+    out["w_lat"] = np.ascontiguousarray(np.concatenate([out[n] for n in INPROJ_LAT_ORDER[kind]], axis=0))
+    return out
