@@ -50,11 +50,13 @@ __global__ void __launch_bounds__(256) compress_kernel(
 
   if (active) {
     const size_t row0 = static_cast<size_t>(b) * S;
-    // Slots in groups of U: the 2U row loads of a group are all issued before any is used,
-    // so a thread keeps 2U independent loads in flight instead of one slot's latency at a time.
+    // Slots in groups of U: the row loads of a group (values, gates and the slot biases) are
+    // all issued before any is used, so a thread keeps them in flight together instead of
+    // paying one slot's latency at a time (a bias load issued at its use would make the wait
+    // for it cover every load issued before it).
     constexpr int U = 8;
     for (int sg = s0; sg < s1; sg += U) {
-      float xv[U][VEC], gv[U][VEC];
+      float xv[U][VEC], gv[U][VEC], bv[U][VEC];
       bool ok[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -66,15 +68,15 @@ __global__ void __launch_bounds__(256) compress_kernel(
         const bool early = x_prev != nullptr && s < m;
         Chunk<T>::template load<VEC>((early ? x_prev : x) + jr * C + c0, xv[u]);
         Chunk<T>::template load<VEC>((early ? gate_prev : gate) + jr * C + c0, gv[u]);
+        if (bias != nullptr)
+          Chunk<float>::template load<VEC>(bias + static_cast<size_t>(ok[u] ? s : 0) * C + c0, bv[u]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
         if (bias != nullptr) {
-          float bv[VEC];
-          Chunk<float>::template load<VEC>(bias + static_cast<size_t>(sg + u) * C + c0, bv);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) gv[u][i] += bv[i];
+          for (int i = 0; i < VEC; ++i) gv[u][i] += bv[u][i];
         }
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
