@@ -73,8 +73,8 @@ constexpr int KL_OFF = LS_OFF + 2 * 64 * 4;          // gather waves' key lists 
 constexpr int kMaxTopk = 1024;                       // key-list capacity on this path
 constexpr int RL_OFF = KL_OFF + 2 * kMaxTopk * 4;    // raw index list of the next query [gather wave]
 constexpr int NK_OFF = RL_OFF + 2 * kMaxTopk * 4;    // key counts of queries [j % 8]
-constexpr int IF_OFF = NK_OFF + 8 * 4;               // RoPE frequencies (double) [32]
-constexpr int kLdsBytes = IF_OFF + 32 * 8;
+constexpr int RT_OFF = NK_OFF + 8 * 4;               // RoPE (cos, sin) of queries [j % 8][32 pairs]
+constexpr int kLdsBytes = RT_OFF + 8 * 32 * 8;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 constexpr float kLazy = 8.f;               // log2-domain headroom before the running max moves
 constexpr double kInv2Pi = 0.15915494309189533576888376337251;
@@ -138,6 +138,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// This lane's id, recomputed where it is used (two instructions) rather than kept live: the
+// optimiser cannot hoist it, so offsets derived from it are not held in registers (or
+// spilled) across the tile loop.
+__device__ __forceinline__ int lane_now() {
+  int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(l));
+  return l;
 }
 
 // Per-query description, computed identically by every wave that needs it.
@@ -228,9 +237,10 @@ attend_mfma_kernel(AttendArgs a) {
   const int G = gridDim.x;
   const bf16_t* qbase = static_cast<const bf16_t*>(a.q);
   int* nk = reinterpret_cast<int*>(lds + NK_OFF);  // compressed-key counts of queries [j % 8]
-  // RoPE frequencies in LDS (read before the first barrier's release by nobody; written here)
-  double* invf = reinterpret_cast<double*>(lds + IF_OFF);
-  if (wave == 0 && lane < R / 2) invf[lane] = a.inv_freq[lane];
+  // (cos, sin) of each rotary pair's angle at a query's position, one row per query [j % 8]:
+  // formed once by a gather wave when it starts the query, read by the score waves (Q
+  // rotation) and the value waves (output counter-rotation, sine negated)
+  float2* rt = reinterpret_cast<float2*>(lds + RT_OFF);
 
   // j-th query of this workgroup, as a rank in the heaviest-first order.  Workgroups are
   // dealt to the 8 XCDs round-robin; with G a multiple of 8, round j gives XCD x the ranks
@@ -250,6 +260,9 @@ attend_mfma_kernel(AttendArgs a) {
     int* kl = reinterpret_cast<int*>(lds + KL_OFF);  // [query parity][kMaxTopk]
     int iq = 0, it = 0;  // issue cursor: query rank, tile
     QInfo qi;
+    // lane i < R/2: frequency of rotary pair i, loaded before any tile or list load is issued
+    const double fq = lane < R / 2 ? a.inv_freq[lane] : 0.0;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     unsigned voff[16];  // lane offset of a row whose chunks are XOR-ed with j
 #pragma unroll
     for (int j = 0; j < 16; ++j) voff[j] = static_cast<unsigned>(lane ^ j) << 4;
@@ -297,6 +310,11 @@ attend_mfma_kernel(AttendArgs a) {
         set_keys(qi, base, a.n_split);
       }
       if (lane == 0) nk[j & 7] = qi.n_keys - qi.n_win;  // compressed keys of query j
+      if (R > 0 && gh == 0 && lane < R / 2) {
+        float c, sn;
+        rope_pair(static_cast<double>(qi.p + a.pos_off), fq, c, sn);
+        rt[(j & 7) * 32 + lane] = make_float2(c, sn);
+      }
     };
     unsigned rlo = 0, rhi = 0;
     auto tile_addr = [&]() {  // lane l < 32: address of key (tb + it)*32 + l of item iq
@@ -402,16 +420,16 @@ attend_mfma_kernel(AttendArgs a) {
     };
     // rotary channels AD-R .. AD-1 = the last R/32 channel steps; this lane's pair i/2 of
     // step ks has index (32 ks + 8 g4 + i - (AD - R)) / 2
-    auto rotate_q = [&](const QInfo& d) {
+    auto rotate_q = [&](int j) {
       if (R == 0) return;
-      const double pos = static_cast<double>(d.p + a.pos_off);
+      const float2* tr = rt + (j & 7) * 32;
 #pragma unroll
       for (int ks = NKS - R / 32; ks < NKS; ++ks) {
         const int pr0 = ((ks * 32 - (AD - R)) >> 1) + 4 * g4;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
-          float c, sn;
-          rope_pair(pos, invf[pr0 + i / 2], c, sn);
+          const float2 cs = tr[pr0 + i / 2];
+          const float c = cs.x, sn = cs.y;
           const float xv = static_cast<float>(qf[ks][i]), yv = static_cast<float>(qf[ks][i + 1]);
           qf[ks][i] = static_cast<__bf16>(xv * c - yv * sn);
           qf[ks][i + 1] = static_cast<__bf16>(xv * sn + yv * c);
@@ -436,7 +454,7 @@ attend_mfma_kernel(AttendArgs a) {
       if (jq >= n_mine) break;  // this step would score tile s + 1
       if (tq == 0) {
         if constexpr (CSA) set_keys(cq, __builtin_amdgcn_readfirstlane(nk[jq & 7]), a.n_split);
-        rotate_q(cq);
+        rotate_q(jq);
         m_run = sink2;
         l_run = 1.f;
       }
@@ -554,17 +572,31 @@ attend_mfma_kernel(AttendArgs a) {
   };
   // epilogue of one query: normalise, counter-rotate (eq. 26), store.  A 32-lane swap pairs
   // the two 4-channel halves so that each lane writes 16 contiguous bytes.
-  auto finish = [&](const QInfo& d, const float (&inv)[2]) {
+  auto finish = [&](const QInfo& d, int j, const float (&inv)[2]) {
     const rsrc_t o_rs = make_rs(static_cast<bf16_t*>(a.out) + (static_cast<size_t>(d.b) * a.T + d.t) * AH * AD,
                                 AH * AD * 2);
-    const double pos = -static_cast<double>(d.p + a.pos_off);  // the same angle, negated
+    // Lane-dependent offsets are formed here, from a fresh lane id: kept live across the
+    // tile loop they were spilled, and each reload's wait (vmcnt) held the next store
+    // behind every store before it.
+    const int ln = lane_now();
+    const int ob = ((ln & 31) * AD + 128 * kq + (ln >> 5) * 8) * 2;  // head block 0, channel block 0
+    const float2* tr = reinterpret_cast<const float2*>(lds + RT_OFF + (j & 7) * 256 + (ln >> 5) * 16);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const unsigned ovoff = static_cast<unsigned>(((32 * hb + l32) * AD + 128 * kq + half * 8) * 2);
+    for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      for (int gp = 0; gp < 2; ++gp) {
+        // this lane's channels: cl0(g2) + 4 half + 0..3, cl0(g2) = 128kq + 32cb + 8(2gp + g2)
+        float2 cs[2][2];  // [g2][pair within the 4 channels], shared by both head blocks
+        const bool rot = R > 0 && 128 * kq + cb * 32 + 16 * gp >= AD - R;
+        if (rot) {
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
+          for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2)
+              cs[g2][i2] = tr[((128 * kq + cb * 32 + 8 * (2 * gp + g2) - (AD - R)) >> 1) + i2];
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
           unsigned w[2][2];
 #pragma unroll
           for (int g2 = 0; g2 < 2; ++g2) {
@@ -572,17 +604,13 @@ attend_mfma_kernel(AttendArgs a) {
             float v[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) v[jj] = o[cb][hb][gq * 4 + jj] * inv[hb];
-            const int cl0 = 128 * kq + cb * 32 + gq * 8;  // channel: cl0 + 4 half + jj
-            if (R > 0 && cl0 >= AD - R) {
-              const int pr0 = (cl0 - (AD - R)) >> 1;  // pair: pr0 + 2 half + i2/2
+            if (rot) {
 #pragma unroll
-              for (int i2 = 0; i2 < 4; i2 += 2) {
-                const double f0 = invf[pr0 + i2 / 2], f1 = invf[pr0 + 2 + i2 / 2];
-                float c, sn;
-                rope_pair(pos, half ? f1 : f0, c, sn);
-                const float xv = v[i2], yv = v[i2 + 1];
-                v[i2] = xv * c - yv * sn;
-                v[i2 + 1] = xv * sn + yv * c;
+              for (int i2 = 0; i2 < 2; ++i2) {
+                const float c = cs[g2][i2].x, sn = -cs[g2][i2].y;
+                const float xv = v[2 * i2], yv = v[2 * i2 + 1];
+                v[2 * i2] = xv * c - yv * sn;
+                v[2 * i2 + 1] = xv * sn + yv * c;
               }
             }
             w[g2][0] = pack_bf16x2(v[0], v[1]);
@@ -596,8 +624,11 @@ attend_mfma_kernel(AttendArgs a) {
           val[1] = s1[0];
           val[2] = s0[1];
           val[3] = s1[1];
-          // lanes >= 32 write group 2gp + 1: their half * 8 channels are part of ovoff
-          __builtin_amdgcn_raw_buffer_store_b128(val, o_rs, ovoff + (cb * 32 + 2 * gp * 8) * 2, 0, 0);
+          // lanes >= 32 write group 2gp + 1: their half * 8 channels are part of ob.  The whole
+          // offset goes in the lane offset (a constant SGPR offset on these stores gave
+          // corrupted output).
+          __builtin_amdgcn_raw_buffer_store_b128(
+              val, o_rs, static_cast<unsigned>(ob + (32 * hb * AD + cb * 32 + 2 * gp * 8) * 2), 0, 0);
           __builtin_amdgcn_sched_barrier(0);  // one group at a time: keeps the epilogue's registers few
         }
       }
@@ -606,11 +637,13 @@ attend_mfma_kernel(AttendArgs a) {
 
   // split mode: the unnormalised output of this key range, counter-rotated (the rotation is
   // linear, so it commutes with the merge), as fp32 rows of the workspace
-  auto finish_part = [&](const QInfo& d, int item) {
-    const double pos = -static_cast<double>(d.p + a.pos_off);
+  auto finish_part = [&](int j, int item) {
+    const int ln = lane_now();  // offsets formed here, as in finish
+    const rsrc_t p_rs = make_rs(a.part + static_cast<size_t>(item) * AH * AD, AH * AD * 4);
+    const int ob = ((ln & 31) * AD + 128 * kq + (ln >> 5) * 4) * 4;  // head block 0, channel 128kq
+    const float2* tr = reinterpret_cast<const float2*>(lds + RT_OFF + (j & 7) * 256 + (ln >> 5) * 16);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      float* po = a.part + (static_cast<size_t>(item) * AH + 32 * hb + l32) * AD + half * 4;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -623,15 +656,17 @@ attend_mfma_kernel(AttendArgs a) {
             const int pr0 = (cl0 - (AD - R)) >> 1;
 #pragma unroll
             for (int i2 = 0; i2 < 4; i2 += 2) {
-              const double f0 = invf[pr0 + i2 / 2], f1 = invf[pr0 + 2 + i2 / 2];
-              float c, sn;
-              rope_pair(pos, half ? f1 : f0, c, sn);
+              const float2 cs = tr[pr0 + i2 / 2];
+              const float c = cs.x, sn = -cs.y;
               const float xv = v[i2], yv = v[i2 + 1];
               v[i2] = xv * c - yv * sn;
               v[i2 + 1] = xv * sn + yv * c;
             }
           }
-          *reinterpret_cast<f32x4_t*>(po + cl0) = f32x4_t{v[0], v[1], v[2], v[3]};
+          const u32x4_t val = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                               __float_as_uint(v[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              val, p_rs, static_cast<unsigned>(ob + (32 * hb * AD + cb * 32 + gq * 8) * 4), 0, 0);
         }
       }
     }
@@ -687,10 +722,11 @@ attend_mfma_kernel(AttendArgs a) {
     }
     if (tp + 1 == cp.n_tiles) {
       if (a.n_split > 1) {
-        finish_part(cp, qid_of(jp));
+        finish_part(jp, qid_of(jp));
       } else {
-        const float inv[2] = {1.f / lsum[par * 64 + l32], 1.f / lsum[par * 64 + 32 + l32]};
-        finish(cp, inv);
+        const int l = lane_now() & 31;
+        const float inv[2] = {1.f / lsum[par * 64 + l], 1.f / lsum[par * 64 + 32 + l]};
+        finish(cp, jp, inv);
       }
       tp = 0;
       if (++jp < n_mine) cp = query_geom<CSA>(a, qid_of(jp));
