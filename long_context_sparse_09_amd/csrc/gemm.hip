@@ -72,7 +72,23 @@ gemm_bt_mfma(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const G
   extern __shared__ __attribute__((aligned(16))) unsigned char glds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  // Tile order: workgroups are dealt to the 8 XCDs round-robin, so each XCD takes a
+  // contiguous range of tile ranks (when the count divides), walked kGroup tile rows at a
+  // time: the workgroups that run together on one XCD then share few A and B tiles in its
+  // L2 (measured ~8 % faster on the output projection than row-major ranks).
+  int tm, tn;
+  {
+    constexpr int kGroup = 4;
+    const int n_t = static_cast<int>(gridDim.x);
+    const int bid = static_cast<int>(blockIdx.x);
+    const int rank = (n_t % 8 == 0) ? (bid % 8) * (n_t / 8) + bid / 8 : bid;
+    const int tiles_m = n_t / tiles_n;
+    const int grp = kGroup * tiles_n;
+    const int first_m = (rank / grp) * kGroup;
+    const int gsz = tiles_m - first_m < kGroup ? tiles_m - first_m : kGroup;
+    tm = first_m + (rank % grp) % gsz;
+    tn = (rank % grp) / gsz;
+  }
   const int g = blockIdx.y;
   const int m0 = tm * GM, n0 = tn * GN;
   // operand descriptors of this batch entry; A covers rows 0..M-1 only (later rows read 0)
