@@ -115,3 +115,19 @@ def test_oproj_full_config_sampled_rows():
                                            W.to_f64(inp["w_b"]), w.o_groups)
     _check(host(mid[SAMPLE]), exact_mid, "bf16", "intermediate (sampled rows)")
     _check(host(out[SAMPLE]), ref_out, "bf16", "output (sampled rows)")
+
+
+@pytest.mark.parametrize("M,N", [(1500, 1024), (2048, 2048), (700, 768)])
+def test_linear_bt_tile_orders(M, N):
+    """Grids whose tile count is a multiple of 8 take the XCD-grouped tile order, including a
+    last group of fewer tile rows (1500 x 1024: 6 x 4 tiles); others take row-major ranks
+    (700 x 768: 3 x 3).  Every output tile must be written once, with its own values."""
+    print(f"[oproj] linear_bt {M} x {N} x 128", flush=True)
+    rng = np.random.default_rng(M + N)
+    x = W.encode(rng.standard_normal((M, 128)).astype(np.float32), "bf16")
+    wt = W.encode((rng.standard_normal((N, 128)) / np.sqrt(128)).astype(np.float32), "bf16")
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.linear_bt(dev(x), dev(wt), y)
+    torch.cuda.synchronize()
+    _, ref = oracle.grouped_out_proj(W.to_f64(x), W.to_f64(wt)[None], np.eye(N), 1)
+    _check(host(y), ref, "bf16", f"linear_bt {M}x{N}")
