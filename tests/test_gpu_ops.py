@@ -236,6 +236,12 @@ def test_index_topk_decode_long_rows():
                few_rows=(1,))
 
 
+def test_index_topk_long_rows_ragged_visibility():
+    # few long rows (the block-per-row top-k): a row with fewer visible entries than k (300),
+    # one with 5100 and a full row (20000) of a 20000-entry pool
+    _topk_case("bf16", 3, 1, 64, 128, 20000, 512, 4, [1199, 20399, 79999], [20000, 20000, 20000], 13)
+
+
 def test_index_topk_small_T_stream_path():
     # T = 3 queries per sequence on the streaming scorer (T < 8), ragged entry counts
     _topk_case("bf16", 2, 3, 64, 128, 3000, 300, 4, [7001, 4096], [1800, 3000], 12)
