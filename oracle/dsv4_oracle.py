@@ -11,7 +11,7 @@ mirrors carry the same text).  Sections cited below are that page's headings:
   "Cache layers"                 - compressor + indexer state
   "DeepseekV4Config"             - parameter meanings (index_topk, sliding_window, ...)
 The page names eqs. 13-17, 26 and 27 but prints none of them.  Each function states the
-reading it computes (R1 ... R16) in its docstring.
+reading it computes (R1 ... R24) in its docstring.
 
 Everything is computed in float64 with no intermediate rounding, except where a caller
 asks to model a storage rounding explicitly (``round_bf16``), which follows the path's
