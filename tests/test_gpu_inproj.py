@@ -123,3 +123,29 @@ SAMPLE = [0, 1, 255, 256, 4095, 4096, 8190, 8191]
 def test_inproj_full_config_sampled_rows():
     w = W.workload(2)
     _run(w, "csa", w.S, sample=SAMPLE)
+
+
+def test_inproj_single_token_full_shape():
+    """One token (a decode step) through the full DeepseekV4Config shapes: a tile row with one
+    live row, every other row of the tile outside the buffers."""
+    w = W.workload(2)
+    _run(w, "csa", 1)
+
+
+def test_linear_bt_multi_eight_segments():
+    print("[inproj] linear_bt_multi 70 x 8 segments x 64", flush=True)
+    rng = np.random.default_rng(10)
+    widths = [32, 64, 32, 96, 32, 32, 64, 32]
+    f32 = [0, 1, 0, 0, 1, 0, 1, 0]
+    N = sum(widths)
+    x = W.encode(rng.standard_normal((70, 64)).astype(np.float32), "bf16")
+    wt = W.encode((rng.standard_normal((N, 64)) / 8.0).astype(np.float32), "bf16")
+    outs = [torch.empty(70, n, dtype=torch.float32 if f else torch.bfloat16, device="cuda")
+            for n, f in zip(widths, f32)]
+    L.linear_bt_multi(dev(x), dev(wt), outs)
+    torch.cuda.synchronize()
+    _, ref = oracle.grouped_out_proj(W.to_f64(x), W.to_f64(wt)[None], np.eye(N), 1)
+    c0 = 0
+    for i, (n, f) in enumerate(zip(widths, f32)):
+        _check(host(outs[i]), ref[:, c0:c0 + n], "fp32" if f else "bf16", f"segment {i}")
+        c0 += n
