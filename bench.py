@@ -470,7 +470,7 @@ def main():
                     help="launch one device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this path runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path would shard by query ranges (one all-gather of the pooled K=V)", file=sys.stderr)
         sys.exit(2)
     import torch
