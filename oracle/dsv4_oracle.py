@@ -29,6 +29,15 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
                            page's printed values (it prints none).
   topk_select              pinned: brute force over a full stable sort, worked example
   visibility               pinned: the page's 16-token worked example
+  csa_index_topk           pinned: queries starting at q_pos0 > 0 and an n_pool below the
+                           visible count against explicit score loops and a stable sort
+  swa_concat               pinned: rows at new_pos0 + i against the closed-form rotation
+  csa_attend / hca_attend  pinned: window buffers whose row 0 is kv_pos0 (at 0, inside the
+                           window, past the query) or that end early, queries at q_pos0 > 0,
+                           and HCA pools capped by n_pool, all against fp64 SDPA with the
+                           explicit mask; the decode layout (one query at L-1, a buffer of the
+                           last W positions, a pool with unused rows) and chunked prefill
+                           (entry ranges, halo buffers, a growing pool) equal the one-shot layer
   attend_query             pinned: torch SDPA (fp64) with explicit K=V and sink column,
                            sink closed forms, eq. 26 shift invariance
   grouped_out_proj         pinned: brute-force loops on tiny shapes, group locality (a group's

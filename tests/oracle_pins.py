@@ -602,4 +602,191 @@ def pin_inproj_token_locality(O):
         assert d[2] > 0 and not np.delete(d, 2).any(), n
 
 
+# ----------------------------------------------------------------------------
+# positions, buffer origins and pool capacities (the arguments decode and chunked prefill use)
+# ----------------------------------------------------------------------------
+
+
+def _rot_rows(x, pos, r, base):
+    """Interleaved-pair rotation of the trailing r channels written out with math.cos/sin per
+    element (independent of the oracle's rope): rows x[i] at positions pos[i]."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    C = x.shape[-1]
+    flat = x.reshape(-1, C)
+    pos = np.broadcast_to(np.asarray(pos, dtype=np.float64), flat.shape[:1])
+    for n in range(flat.shape[0]):
+        for i in range(r // 2):
+            ang = pos[n] * base ** (-2.0 * i / r)
+            a, b = flat[n, C - r + 2 * i], flat[n, C - r + 2 * i + 1]
+            flat[n, C - r + 2 * i] = a * math.cos(ang) - b * math.sin(ang)
+            flat[n, C - r + 2 * i + 1] = a * math.sin(ang) + b * math.cos(ang)
+    return flat.reshape(x.shape)
+
+
+def _dense_ref(q_rows, q_pos, keys, keep, sink, r, base, D):
+    """Masked attention of queries at sequence indices q_pos over rotated keys, by torch SDPA in
+    fp64 (K and V separate but equal, sink as a zero-value column), counter-rotated."""
+    T, H = q_rows.shape[:2]
+    q_rot = np.stack([_rot_rows(q_rows[t], q_pos[t], r, base) for t in range(T)])
+    o = _sdpa_reference(None, q_rot, keys, keep, sink, 1.0 / math.sqrt(D))
+    return np.stack([_rot_rows(o[t], -q_pos[t], r, base) for t in range(T)])
+
+
+def pin_window_buffer_origin_and_clipping(O):
+    """A window buffer whose row 0 is sequence index kv_pos0 and which holds S_buf rows: the
+    query at p attends the rows of sequence indices max(0, p-W+1) .. p that the buffer holds
+    and nothing else (origin at 0, inside the window, past some queries; a buffer that ends
+    early), for queries starting at q_pos0 > 0 too."""
+    rng = RNG(41)
+    S, H, D, r, W, base = 30, 2, 8, 4, 6, 10000.0
+    q = rng.standard_normal((1, S, H, D))
+    kv = rng.standard_normal((S, D))
+    sink = rng.standard_normal(H)
+    rot = _rot_rows(kv, np.arange(S), r, base)
+    for kv_pos0, S_buf in ((0, S), (3, S - 3), (12, 10), (25, 5), (9, 2)):
+        buf = rot[kv_pos0:kv_pos0 + S_buf][None]
+        for q_pos0 in (0, 7):
+            qs = q[:, q_pos0:]
+            p = q_pos0 + np.arange(S - q_pos0)
+            keep = np.zeros((len(p), S), dtype=bool)
+            for n, pt in enumerate(p):
+                for j in range(max(0, pt - W + 1), pt + 1):
+                    keep[n, j] = kv_pos0 <= j < kv_pos0 + S_buf
+            ref = _dense_ref(qs[0], p, rot, keep, sink, r, base, D)
+            got = O.hca_attend(qs, buf, [kv_pos0], None, None, 128, sink, [q_pos0], W, r, base)
+            _close(got[0], ref, 1e-12, f"window buffer at {kv_pos0} ({S_buf} rows), q from {q_pos0}")
+            # the CSA call takes the same window rows (with no entry selected)
+            none = np.full((1, len(p), 2), -1)
+            got_c = O.csa_attend(qs, buf, [kv_pos0], np.zeros((1, 1, D)), none, sink, [q_pos0], W,
+                                 r, base)
+            _close(got_c[0], ref, 1e-12, f"CSA window buffer at {kv_pos0}, q from {q_pos0}")
+
+
+def pin_index_topk_positions_and_capacity(O):
+    """csa_index_topk for queries starting at q_pos0 > 0 and pools whose valid count n_pool
+    cuts the visible entries: explicit score loops and a stable library sort."""
+    rng = RNG(42)
+    B, T, nI, cI, m, N_cap = 2, 9, 3, 5, 4, 12
+    q_idx = rng.standard_normal((B, T, nI, cI))
+    w_idx = rng.standard_normal((B, T, nI))
+    k_pool = rng.standard_normal((B, N_cap, cI))
+    q_pos0, n_pool = [17, 30], [5, 12]
+    for k in (3, 6):
+        idx, sc = O.csa_index_topk(q_idx, w_idx, k_pool, q_pos0, n_pool, m, k)
+        for b in range(B):
+            for t in range(T):
+                V = min((q_pos0[b] + t + 1) // m, n_pool[b])
+                s = np.zeros(V)
+                for w in range(V):
+                    for h in range(nI):
+                        dot = sum(q_idx[b, t, h, c] * k_pool[b, w, c] for c in range(cI))
+                        s[w] += w_idx[b, t, h] * max(dot, 0.0)
+                ref = np.sort(np.argsort(-s, kind="stable")[:min(k, V)])
+                row = idx[b, t]
+                assert np.array_equal(row[:len(ref)], ref) and np.all(row[len(ref):] == -1), \
+                    (k, b, t, row, ref)
+                _close(sc[b, t, :len(ref)], s[ref], 1e-12, "scores of the kept entries")
+
+
+def pin_swa_positions(O):
+    """swa_concat rotates row i of sequence b at new_pos0[b] + i + offset (closed form)."""
+    rng = RNG(43)
+    kv = rng.standard_normal((2, 5, 6))
+    new_pos0, r, base, off = [0, 37], 4, 100.0, 3
+    got = O.swa_concat(kv, new_pos0, r, base, off)
+    for b in range(2):
+        for i in range(5):
+            _close(got[b, i], _rot_rows(kv[b, i], new_pos0[b] + i + off, r, base), 1e-12,
+                   f"window row {b},{i}")
+
+
+def pin_hca_pool_capacity(O):
+    """hca_attend with n_pool below the pool's rows: entry w is visible to the query at p iff
+    w < min((p+1)//m, n_pool); fp64 SDPA with that mask."""
+    rng = RNG(44)
+    S, H, D, r, m, W, base = 40, 2, 8, 4, 8, 5, 10000.0
+    q = rng.standard_normal((1, S, H, D))
+    kv = rng.standard_normal((S, D))
+    pool = rng.standard_normal((1, 5, D))
+    sink = rng.standard_normal(H)
+    rot = _rot_rows(kv, np.arange(S), r, base)
+    for n_pool in (3, 5, 0):
+        got = O.hca_attend(q, rot[None], [0], pool, [n_pool], m, sink, [0], W, r, base)
+        keys = np.concatenate([rot, pool[0]], axis=0)
+        keep = np.zeros((S, S + 5), dtype=bool)
+        for t in range(S):
+            keep[t, max(0, t - W + 1):t + 1] = True
+            for w in range(min((t + 1) // m, n_pool)):
+                keep[t, S + w] = True
+        ref = _dense_ref(q[0], np.arange(S), keys, keep, sink, r, base, D)
+        _close(got[0], ref, 1e-12, f"HCA with n_pool = {n_pool}")
+
+
+def pin_decode_layout_equals_prefill_row(O):
+    """The decode layout (one query at L-1, a window buffer holding positions L-W .. L-1, a
+    pool whose first L//m rows are valid and the rest arbitrary) gives row L-1 of the one-shot
+    prefill layer, for CSA and HCA."""
+    inp = _csa_inputs(45, S=33)
+    cfg = _Cfg(m=4, r=4, base=10000.0, k=3, W=5, m_hca=8)
+    out, idx, aux = O.csa_layer(inp, cfg)
+    junk = RNG(46).standard_normal
+    for L in (33, 20, 4, 3):
+        t = L - 1
+        n = L // cfg.m
+        win = aux["kv_win"][:, L - cfg.W:L] if L >= cfg.W else aux["kv_win"][:, :L]
+        kv0 = max(L - cfg.W, 0)
+        k_pool = np.concatenate([aux["k_pool"][:, :n], junk((1, 4, aux["k_pool"].shape[2]))], axis=1)
+        pool = np.concatenate([aux["pool"][:, :n], junk((1, 4, aux["pool"].shape[2]))], axis=1)
+        di, _ = O.csa_index_topk(inp["q_idx"][:, t:t + 1], inp["w_idx"][:, t:t + 1], k_pool, [t], [n],
+                                 cfg.m, cfg.k)
+        assert np.array_equal(di[0, 0], idx[0, t]), (L, di[0, 0], idx[0, t])
+        do = O.csa_attend(inp["q"][:, t:t + 1], win, [kv0], pool, di, inp["sink"], [t], cfg.W, cfg.r,
+                          cfg.base)
+        _close(do[0, 0], out[0, t], 1e-12, f"CSA decode row at L={L}")
+    hout, haux = O.hca_layer(inp, cfg)
+    hp = haux["pool"]
+    for L in (33, 16, 9):
+        t, n = L - 1, L // cfg.m_hca
+        pool = np.concatenate([hp[:, :n], junk((1, 3, hp.shape[2]))], axis=1)
+        do = O.hca_attend(inp["q"][:, t:t + 1], haux["kv_win"][:, L - cfg.W:L], [L - cfg.W], pool, [n],
+                          cfg.m_hca, inp["sink"], [t], cfg.W, cfg.r, cfg.base)
+        _close(do[0, 0], hout[0, t], 1e-12, f"HCA decode row at L={L}")
+
+
+def pin_chunked_prefill_equals_one_shot(O):
+    """Prefill in chunks of queries (entries pooled chunk by chunk through entry ranges, each
+    chunk's window buffer starting W-1 rows before it, the pool's valid count growing) equals
+    the one-shot layer, for CSA and HCA."""
+    inp = _csa_inputs(47, S=33)
+    cfg = _Cfg(m=4, r=4, base=10000.0, k=3, W=5, m_hca=8)
+    out, idx, aux = O.csa_layer(inp, cfg)
+    hout, haux = O.hca_layer(inp, cfg)
+    S = 33
+    D = inp["kv"].shape[2]
+    pool = np.zeros((1, S // cfg.m, D))
+    k_pool = np.zeros((1, S // cfg.m, inp["k_idx"].shape[2]))
+    hpool = np.zeros((1, S // cfg.m_hca, D))
+    got, hgot = [], []
+    for c0, c1 in ((0, 12), (12, 25), (25, 33)):
+        e0, e1 = c0 // cfg.m, c1 // cfg.m
+        pool[:, e0:e1] = O.csa_compress(inp["kv"][:, :c1], inp["gate"][:, :c1], inp["bias"], cfg.m,
+                                        True, cfg.r, cfg.base, 0, e0, e1)
+        k_pool[:, e0:e1] = O.csa_compress(inp["k_idx"][:, :c1], inp["g_idx"][:, :c1], inp["bias_idx"],
+                                          cfg.m, True, 0, 10000.0, 0, e0, e1)
+        h0, h1 = c0 // cfg.m_hca, c1 // cfg.m_hca
+        hpool[:, h0:h1] = O.csa_compress(inp["kv"][:, :c1], inp["gate"][:, :c1], inp["bias_hca"],
+                                         cfg.m_hca, False, cfg.r, cfg.base, 0, h0, h1)
+        kv0 = max(c0 - cfg.W + 1, 0)
+        win = O.swa_concat(inp["kv"][:, kv0:c1], [kv0], cfg.r, cfg.base)
+        ci, _ = O.csa_index_topk(inp["q_idx"][:, c0:c1], inp["w_idx"][:, c0:c1], k_pool, [c0], [e1],
+                                 cfg.m, cfg.k)
+        assert np.array_equal(ci[0], idx[0, c0:c1])
+        got.append(O.csa_attend(inp["q"][:, c0:c1], win, [kv0], pool, ci, inp["sink"], [c0], cfg.W,
+                                cfg.r, cfg.base)[0])
+        hgot.append(O.hca_attend(inp["q"][:, c0:c1], win, [kv0], hpool, [h1], cfg.m_hca, inp["sink"],
+                                 [c0], cfg.W, cfg.r, cfg.base)[0])
+    _close(np.concatenate(got), out[0], 1e-12, "chunked CSA")
+    _close(np.concatenate(hgot), hout[0], 1e-12, "chunked HCA")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -255,11 +255,19 @@ def test_index_topk_exact_ties():
 # ---------------------------------------------------------------------------- attention
 
 def _attend_case(dt, csa, B, T, H, D, r, Wn, S_kv, kv_pos0, q_pos0, N_cap, k=0, n_pool=None,
-                 m_hca=16, seed=20, shuffle_invalid=False, split=False):
+                 m_hca=16, seed=20, shuffle_invalid=False, split=False, full_lists=False):
     q = normal("q", (B, T, H, D), seed)
     win = normal("win", (B, S_kv, D), seed)
     pool = normal("pool", (B, max(N_cap, 1), D), seed)[:, :N_cap]
     sink = normal("sink", (H,), seed).astype(np.float32)
+    if csa:
+        topk = W.random_index_lists(seed, "topk", B, T, k, N_cap, shuffle_invalid, full_lists)
+        if full_lists and k % 4:
+            # the entries of the slots past the last multiple of 4 get large rows, so that
+            # attending any other entry in their place moves the output far
+            for b in range(B):
+                tail = topk[b, :, k & ~3:k]
+                pool[b, np.unique(tail[tail >= 0])] *= 3.0
     qs, ws_, ps = enc(q, dt), enc(win, dt), enc(pool, dt)
     base, off = 10000.0, 11
     out = torch.empty(B, T, H, D, dtype=torch_dtype(dt), device="cuda")
@@ -270,7 +278,6 @@ def _attend_case(dt, csa, B, T, H, D, r, Wn, S_kv, kv_pos0, q_pos0, N_cap, k=0, 
         assert nb > 0, "the split path should apply to this few queries"
         wsp = torch.empty(nb, dtype=torch.uint8, device="cuda")
     if csa:
-        topk = W.random_index_lists(seed, "topk", B, T, k, N_cap, shuffle_invalid)
         L.csa_attend(dev(qs), dev(ws_), i32(kv_pos0), pool_t, dev(topk), dev(sink), i32(q_pos0),
                      out, Wn, r, base, off, workspace=wsp)
         ref = oracle.csa_attend(W.to_f64(qs), W.to_f64(ws_), kv_pos0, W.to_f64(ps), topk, sink,
@@ -345,6 +352,16 @@ def test_split_attend_short_and_empty_queries():
 def test_split_attend_csa_two_queries_per_sequence():
     _attend_case("bf16", True, 3, 2, 64, 512, 64, 128, 256, [0, 100, 7], [200, 300, 40], 300,
                  k=128, seed=30, split=True, shuffle_invalid=True)
+
+
+@pytest.mark.parametrize("k", [510, 6, 509])
+@pytest.mark.parametrize("split", [False, True])
+def test_csa_attend_list_length_not_multiple_of_4(k, split):
+    # full lists whose last slots (k & ~3 .. k - 1) hold valid entries: the list copy into LDS
+    # must deliver those slots, not zeros (entry 0) from a load that crosses the list's end
+    B, T = (3, 2) if split else (1, 24)
+    _attend_case("bf16", True, B, T, 64, 512, 64, 128, 700, [0] * B, [600] * B, 700, k=k,
+                 seed=31 + k, split=split, full_lists=True)
 
 
 # ---------------------------------------------------------------------------- errors

@@ -1,6 +1,7 @@
 """Plant plausible mistakes in a copy of the oracle (on the CPU) and check each trips a pin.
 
-Each mutation is a textual edit of the oracle's source, executed as a fresh module; the
+Each mutation is a textual edit of the oracle's source (an anchor that must occur exactly
+once, or the stated number of times, all of them replaced), executed as a fresh module; the
 real oracle is untouched.  A mutation that no pin catches would mean the pins leave that
 part of the oracle unchecked.
 """
@@ -65,14 +66,35 @@ MUTATIONS = {
                                       'lat = round_bf16(out["c_q"])')],
     "inproj_indexer_query_from_query": [("out[name] = lat @ W[name].T",
                                          "out[name] = lat @ W[name].T if name == \"q\" else out[\"q\"][:, :W[name].shape[0]]")],
+    # window buffer origin and clipping (decode rings, chunk halos)
+    "window_start_clip_dropped": [("r0 = max(lo - kv_pos0_b, 0)", "r0 = lo - kv_pos0_b")],
+    "window_end_clip_off_by_one": [("r1 = min(qpos + 1 - kv_pos0_b, kv_win_b.shape[0])",
+                                    "r1 = min(qpos + 1 - kv_pos0_b, kv_win_b.shape[0] - 1)")],
+    "window_buffer_origin_ignored": [("r0 = max(lo - kv_pos0_b, 0)", "r0 = max(lo, 0)"),
+                                     ("r1 = min(qpos + 1 - kv_pos0_b, kv_win_b.shape[0])",
+                                      "r1 = min(qpos + 1, kv_win_b.shape[0])")],
+    # query start positions and pool capacities
+    "index_q_pos0_ignored": [("V = n_visible(int(q_pos0[b]) + t, m, int(n_pool[b]))",
+                              "V = n_visible(t, m, int(n_pool[b]))")],
+    "index_n_pool_cap_dropped": [("V = n_visible(int(q_pos0[b]) + t, m, int(n_pool[b]))",
+                                  "V = n_visible(int(q_pos0[b]) + t, m)")],
+    "swa_new_pos0_ignored": [("pos = new_pos0[b] + np.arange(S_new) + pos_offset",
+                              "pos = np.arange(S_new) + pos_offset")],
+    "hca_n_pool_cap_dropped": [("V = n_visible(qpos, m_hca, npb)", "V = n_visible(qpos, m_hca)")],
+    "attend_q_pos0_ignored": [("qpos = int(q_pos0[b]) + t", "qpos = t", 2)],
+    "hca_q_pos0_off_by_one": [("V = n_visible(qpos, m_hca, npb)", "V = n_visible(qpos - 1, m_hca, npb)")],
+    "compress_entry_range_ignored": [("for w in range(entry_begin, entry_end):",
+                                      "for w in range(0, entry_end - entry_begin):")],
 }
 
 
 def _mutant(edits):
     with open(SRC) as f:
         text = f.read()
-    for old, new in edits:
-        assert text.count(old) == 1, f"mutation anchor not unique/absent: {old!r}"
+    for edit in edits:
+        old, new = edit[:2]
+        n = edit[2] if len(edit) > 2 else 1  # occurrences the edit must find (all replaced)
+        assert text.count(old) == n, f"mutation anchor found {text.count(old)} times, not {n}: {old!r}"
         text = text.replace(old, new)
     spec = importlib.util.spec_from_loader("oracle_mutant", loader=None)
     mod = importlib.util.module_from_spec(spec)

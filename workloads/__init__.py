@@ -330,15 +330,16 @@ def decode_inputs(w: Workload, n_seq: Optional[int] = None, pool_rows: Optional[
 
 
 def random_index_lists(seed: int, name: str, B: int, T: int, k: int, N: int,
-                       shuffle: bool = False) -> np.ndarray:
-    """int32 [B, T, k] lists of distinct entries < N, a random number (0..min(k, N)) per row,
-    padded with -1 (after the valid entries, or scattered among them when shuffle=True).
-    Synthetic inputs for the attention call, which takes index lists as given."""
+                       shuffle: bool = False, full: bool = False) -> np.ndarray:
+    """int32 [B, T, k] lists of distinct entries < N, a random number (0..min(k, N)) per row
+    (exactly min(k, N) with full=True), padded with -1 (after the valid entries, or scattered
+    among them when shuffle=True).  Synthetic inputs for the attention call, which takes index
+    lists as given."""
     gen = _block_gen(seed, 0, name, 0)
     out = np.full((B, T, k), -1, dtype=np.int32)
     for b in range(B):
         for t in range(T):
-            n = int(gen.integers(0, min(k, N) + 1))
+            n = min(k, N) if full else int(gen.integers(0, min(k, N) + 1))
             out[b, t, :n] = gen.choice(N, size=n, replace=False)
             if shuffle:
                 gen.shuffle(out[b, t])
