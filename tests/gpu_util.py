@@ -95,3 +95,27 @@ def check_topk_row(gpu_row: np.ndarray, scores: np.ndarray, k: int, what: str) -
         assert abs(s[x] - s_k) <= band and not exact_tie, \
             f"{what}: entry {x} score {s[x]!r} vs k-th {s_k!r} (band {band:.3e})"
     return len(diff) // 2
+
+
+def check_keys(gpu_keys, ref_keys, dt: str, what: str):
+    """Compressed keys computed on the GPU against the oracle's: within one bf16 ulp on the
+    bf16 path (storage rounding of an fp32 result), 1e-5 * max|ref| on the fp32 path."""
+    if dt == "bf16":
+        assert_bf16_ulp(gpu_keys, ref_keys, what)
+    else:
+        assert_close(gpu_keys, ref_keys, "fp32", what)
+
+
+def staged_topk_row(gpu_row, q_idx_t, w_idx_t, gpu_keys, k: int, what: str) -> int:
+    """Top-k stage on its own: the oracle scores the query against the GPU's compressed keys
+    gpu_keys [V, cI] (already held to the oracle's own keys by check_keys), so both sides
+    select from the same bf16 values, and the GPU's list must be that selection (ties to the
+    lower index; swaps only inside the relative band of the k-th score)."""
+    s = oracle_index_scores(q_idx_t, w_idx_t, gpu_keys)
+    return check_topk_row(gpu_row, s, k, what)
+
+
+def oracle_index_scores(q_idx_t, w_idx_t, keys):
+    import oracle
+
+    return oracle.index_scores(q_idx_t, w_idx_t, keys)

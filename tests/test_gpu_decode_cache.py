@@ -11,15 +11,18 @@ The prefill lengths mix a sequence shorter than one entry, one shorter than the 
 ones past the top-k size; the steps close CSA entries (every 4 tokens, the first one with
 absent overlap positions), HCA entries (crossing a multiple of 128) and refill the window
 buffer (every G steps).  Tolerances as for the layer tests: outputs |d| <= 2e-2 * max|ref|
-per step, pool and window rows within one bf16 ulp of the exact value, top-k sets exact
-except inside the 1e-4 relative band of the k-th score.
+per step, pool and window rows within one bf16 ulp of the exact value.  CSA parity is
+stage-wise at every step: the cache's indexer keys are held to the oracle's (one bf16 ulp),
+the oracle scores the cache's keys and the GPU's top-k list must be that selection (exact
+except inside the 1e-4 relative band of the k-th score), and the oracle's attention runs on
+the GPU's list.
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads as W
-from gpu_util import assert_bf16_ulp, assert_close, check_topk_row, dev, host
+from gpu_util import assert_bf16_ulp, assert_close, check_keys, dev, host, staged_topk_row
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +80,6 @@ def _run(kind, L0, n_steps, G, n_cap=None):
         pool = oracle.csa_compress(kv, W.to_f64(inp["gate"]), inp["bias_hca"], w.m_hca, False, w.r,
                                    w.base)
     pool_r = None if pool is None else R(pool)
-    k_pool_r = None if k_pool is None else R(k_pool)
     excused = 0
     for j in range(n_steps):
         qa = _query_rows(w, ell, kind, L0, j)
@@ -86,6 +88,7 @@ def _run(kind, L0, n_steps, G, n_cap=None):
         tok.update({n: dev(a) for n, a in qa.items()})
         out = host(cache.step(tok))
         gpu_idx = cache.topk_idx.cpu().numpy() if kind == "csa" else None
+        gpu_keys = host(cache.k_pool) if kind == "csa" else None
         refs = []
         for b in range(B):
             t = L0[b] + j  # the query's sequence index; L = t + 1 tokens so far
@@ -95,12 +98,11 @@ def _run(kind, L0, n_steps, G, n_cap=None):
             if kind == "csa":
                 N = min((t + 1) // w.m, n_cap)
                 qi = W.to_f64(qa["q_idx"][b:b + 1])
-                s = oracle.index_scores(qi[0, 0], qa["w_idx"][b, 0], k_pool_r[b, :N])
-                excused += check_topk_row(gpu_idx[b, 0], s, gpu_idx.shape[2], f"b={b} t={t}")
-                idx, _ = oracle.csa_index_topk(qi, qa["w_idx"][b:b + 1], k_pool_r[b:b + 1], [t],
-                                               [N], w.m, cache.k_eff)
-                ref = oracle.csa_attend(q, win, [lo], pool_r[b:b + 1], idx, inp["sink"], [t], w.W,
-                                        w.r, w.base)
+                check_keys(gpu_keys[b, :N], k_pool[b, :N], "bf16", f"indexer keys b={b} t={t}")
+                excused += staged_topk_row(gpu_idx[b, 0], qi[0, 0], qa["w_idx"][b, 0],
+                                           gpu_keys[b, :N], gpu_idx.shape[2], f"b={b} t={t}")
+                ref = oracle.csa_attend(q, win, [lo], pool_r[b:b + 1], gpu_idx[b:b + 1], inp["sink"],
+                                        [t], w.W, w.r, w.base)
             elif kind == "hca":
                 ref = oracle.hca_attend(q, win, [lo], pool_r[b:b + 1], [n_cap], w.m_hca,
                                         inp["sink"], [t], w.W, w.r, w.base)
