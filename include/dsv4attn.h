@@ -18,7 +18,8 @@
  * Conventions shared by every entry point
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the caller owns
  *     all buffers.  The library never allocates or frees device memory; scratch memory is
- *     passed in explicitly (csa_index_topk's workspace).
+ *     passed in explicitly (csa_index_topk's workspace), except for the fixed static array
+ *     of csa_index_topk_noalloc.
  *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue work and
  *     return; results are ready when the stream reaches them.
  *   - Tensors are dense row-major with the channel axis innermost.  dtype DSV4_FP32 or
@@ -166,6 +167,25 @@ int csa_index_topk(const void* q_idx, const float* w_idx, const void* k_pool, co
                    const int* n_pool, int* topk_idx, float* topk_score, int B, int T, int nI,
                    int cI, int N_cap, int m, int k, void* workspace, size_t workspace_bytes,
                    int dtype, void* stream);
+
+/*
+ * csa_index_topk_noalloc - csa_index_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and errors as csa_index_topk, without the workspace: the score
+ * scratch is a static device array of DSV4_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library,
+ * one copy per GPU the library runs on, held until the process ends.  The call allocates and
+ * frees nothing.  Requests whose scratch, csa_index_topk_workspace_size(B, T, N_cap, k), exceeds
+ * that size return DSV4_ERR_UNSUPPORTED before anything is enqueued (for example 64 decode
+ * queries over 32768 entries, 8 MiB, fit; a 4096-query prefill chunk over 8192 entries does not).  All calls on one
+ * GPU share its array: calls that overlap in time on one GPU (unordered streams or threads)
+ * race and must be serialised by the caller; stream-ordered calls are safe.
+ */
+#define DSV4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int csa_index_topk_noalloc(const void* q_idx, const float* w_idx, const void* k_pool,
+                           const int* q_pos0, const int* n_pool, int* topk_idx, float* topk_score,
+                           int B, int T, int nI, int cI, int N_cap, int m, int k, int dtype,
+                           void* stream);
 
 /*
  * swa_concat - rotate raw K=V rows into the sliding-window buffer ("Hybrid attention

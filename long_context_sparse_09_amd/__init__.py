@@ -13,7 +13,7 @@ from typing import Optional
 from . import _lib
 
 __all__ = ["csa_compress", "compressor_cache_update", "csa_index_topk",
-           "csa_index_topk_workspace_size", "swa_concat", "csa_attend", "hca_attend",
+           "csa_index_topk_workspace_size", "csa_index_topk_noalloc", "NOALLOC_SCRATCH_BYTES", "swa_concat", "csa_attend", "hca_attend",
            "attend_workspace_size", "grouped_out_proj", "linear_bt", "linear_bt_multi", "input_projections", "attention_mask_dump",
            "abi_version", "DSV4Error", "lib"]
 
@@ -136,6 +136,21 @@ def csa_index_topk(q_idx, w_idx, k_pool, q_pos0, n_pool, topk_idx, topk_score, m
         _ptr(q_idx), _ptr(w_idx), _ptr(k_pool), _ptr(q_pos0), _ptr(n_pool), _ptr(topk_idx),
         _ptr(topk_score), B, T, nI, cI, N_cap, m, k, _ptr(workspace), nbytes, _dtype(q_idx),
         _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def csa_index_topk_noalloc(q_idx, w_idx, k_pool, q_pos0, n_pool, topk_idx, topk_score, m: int,
+                           stream=None) -> None:
+    """csa_index_topk with the library's static score scratch (no workspace argument); raises
+    DSV4Error (status 2) when B*T*N_cap*4 bytes exceed NOALLOC_SCRATCH_BYTES."""
+    B, T, nI, cI = q_idx.shape
+    N_cap = k_pool.shape[1]
+    k = topk_idx.shape[2]
+    _check("csa_index_topk_noalloc", lib().csa_index_topk_noalloc(
+        _ptr(q_idx), _ptr(w_idx), _ptr(k_pool), _ptr(q_pos0), _ptr(n_pool), _ptr(topk_idx),
+        _ptr(topk_score), B, T, nI, cI, N_cap, m, k, _dtype(q_idx), _stream(stream)))
 
 
 def swa_concat(kv_raw, kv_win, kv_pos0, new_pos0, rope_dim: int, rope_theta: float,

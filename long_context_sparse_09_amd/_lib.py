@@ -44,6 +44,8 @@ SIGNATURES = {
     "csa_index_topk": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_size_t,
                         c_int, c_void_p], c_int),
+    "csa_index_topk_noalloc": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p], c_int),
     "swa_concat": ([c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                     c_double, c_ll, c_int, c_void_p], c_int),
     "attend_workspace_size": ([c_int, c_int, c_int, c_int], c_size_t),

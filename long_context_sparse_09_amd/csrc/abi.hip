@@ -27,6 +27,13 @@ int ok() {
   return DSV4_OK;
 }
 
+}  // namespace
+
+// Status reporting for entry points defined in other source files of the library.
+int dsv4::report_error(int status, const char* msg) { return fail(status, "%s", msg); }
+
+namespace {
+
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DSV4_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
   return ok();

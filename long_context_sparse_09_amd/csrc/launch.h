@@ -8,6 +8,9 @@
 
 namespace dsv4 {
 
+// Records msg as the calling thread's last error detail and returns status.
+int report_error(int status, const char* msg);
+
 // x_prev / gate_prev: NULL, or the second projection the earlier half of each overlapping
 // window reads (overlap only).
 hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
