@@ -272,27 +272,24 @@ attend_mfma_kernel(AttendArgs a) {
     // current tile are the only ones allowed in flight (vmcnt(16)) it has landed.
     constexpr int NC = kMaxTopk / 64;
     const int* rl = reinterpret_cast<const int*>(lds + RL_OFF) + gh * kMaxTopk;
-    // The descriptor ends at the list's last entry.  With k a multiple of 4 every 16-byte
-    // lane load lies wholly inside it or wholly past it; otherwise one load would straddle
-    // the end, and a straddling load may read as zeros (entry 0) for its valid entries too,
-    // so such lists move one 4-byte entry per lane.
+    // 16-byte lane loads copy entries 0 .. k4-1 (k4 = k rounded down to a multiple of 4);
+    // lanes at or past k4 are masked off, so no load straddles the end of the list (a load
+    // crossing the descriptor's end may read as zeros, entry 0, for its valid entries too).
+    // The k - k4 remaining entries move as one 4-byte load per lane, into slots no 16-byte
+    // load writes.
     auto list_dma = [&](int j) {
       const QInfo d = query_geom<CSA>(a, qid_of(j));
-      const rsrc_t idx_rs = make_rs(a.topk_idx + (static_cast<size_t>(d.b) * a.T + d.t) * a.k,
-                                    static_cast<unsigned>(a.k) * 4u);
-      if ((a.k & 3) == 0) {
+      const int* row = a.topk_idx + (static_cast<size_t>(d.b) * a.T + d.t) * a.k;
+      const int k4 = a.k & ~3;
+      const rsrc_t idx_rs = make_rs(row, static_cast<unsigned>(a.k) * 4u);
 #pragma unroll
-        for (int c = 0; c < kMaxTopk / 256; ++c)  // 256 entries (1 KB) per instruction
-          if (c * 256 < a.k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(idx_rs, (lds_void*)(rl + c * 256), 16,
-                                                     static_cast<unsigned>(c * 1024 + lane * 16), 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int c = 0; c < kMaxTopk / 64; ++c)  // 64 entries (256 B) per instruction
-          if (c * 64 < a.k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(idx_rs, (lds_void*)(rl + c * 64), 4,
-                                                     static_cast<unsigned>(c * 256 + lane * 4), 0, 0, 0);
-      }
+      for (int c = 0; c < kMaxTopk / 256; ++c)  // 256 entries (1 KB) per instruction
+        if (c * 256 < k4 && c * 256 + lane * 4 < k4)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(idx_rs, (lds_void*)(rl + c * 256), 16,
+                                                   static_cast<unsigned>(c * 1024 + lane * 16), 0, 0, 0);
+      if (k4 != a.k && lane < a.k - k4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(idx_rs, (lds_void*)(rl + k4), 4,
+                                                 static_cast<unsigned>(k4 * 4 + lane * 4), 0, 0, 0);
     };
     if constexpr (CSA) list_dma(0);
     auto load_query = [&](int j) {
