@@ -17,7 +17,7 @@ Kernel timing protocol: every launch is bracketed by HIP events on the stream it
 on (torch's current stream, which every library call uses); at least 10 launches per kernel
 after 3 warm-ups; median, minimum and mean are reported and fractions use the median.  Before
 each timed launch of a kernel whose working set is below 512 MB the 256 MB Infinity Cache and
-the L2s are flushed by writing a 1 GiB buffer (outside the events), so such kernels read HBM,
+the L2s are flushed by reading a 1 GiB buffer (outside the events), so such kernels read HBM,
 not a warm cache.  Decode steps are timed the same way, one step per event pair, flushed.
 
 "roofline" is for the dominant kernel (csa_attend): algorithmic flops per launch over the
@@ -113,10 +113,13 @@ class Clock:
 
     def __init__(self, torch):
         self.torch = torch
-        self.flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
 
     def flush(self):
-        self.flush_buf.fill_(1.0)  # 1 GiB of writes: evicts the Infinity Cache and the L2s
+        # 1 GiB of reads evicts the Infinity Cache and the L2s with clean lines (a write would
+        # leave dirty lines whose write-back overlaps the timed launch)
+        self.flush_buf.sum()
 
     def launches(self, fn, reps=KERNEL_REPS, warm=3, flush=True):
         """Durations (ms) of `reps` launches of fn, each between two events."""

@@ -150,11 +150,248 @@ static hipError_t compress_t(const void* x, const void* gate, const void* x_prev
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// compress, overlapping windows at a small rate (CSA, m = M, bf16, VEC = 8 channels a lane):
+// register-resident windows.  The tokens of an entry's window form two blocks of M tokens,
+// [(w-1)M, wM) (slots 0..M-1) and [wM, (w+1)M) (slots M..2M-1), and each block belongs to two
+// consecutive entries.  A stream (the G = C/8 lanes of one row) pools E consecutive entries:
+// it loads its E + 1 blocks once, all up front, so every token is read from memory once per
+// stream (neighbouring streams share one block, fetched into the same XCD's L2: consecutive
+// streams are dealt to one XCD), and keeps them in registers.  Per entry and channel the
+// softmax is taken in two passes over the 2M slots (maximum, then exponentials), with the
+// slot biases pre-scaled to the log2 domain once per stream.  One wavefront per block, no
+// barriers besides the RoPE table's.
+// ---------------------------------------------------------------------------
+template <int M, int E>
+__global__ void __launch_bounds__(64) compress_window_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ gate, const float* __restrict__ bias,
+    bf16_t* __restrict__ pool, int S, int C, int e0, int e1, int N_cap, int r, const RopeFreq rf,
+    long long pos_off, int G, int n_streams, int blocks_per_xcd) {
+  constexpr int VEC = 8;
+  constexpr int NB = E + 1;  // token blocks of a stream
+  __shared__ double inv_freq[kMaxRope / 2];
+  for (int i = threadIdx.x; i < r / 2; i += 64) inv_freq[i] = rf.inv[i];
+  __syncthreads();
+  // consecutive logical blocks on one XCD (the hardware deals workgroups to XCDs round-robin)
+  const int lb = (blockIdx.x % 8) * blocks_per_xcd + blockIdx.x / 8;
+  const int spb = 64 / G;  // streams per block
+  const int stream = lb * spb + static_cast<int>(threadIdx.x) / G;
+  if (stream >= n_streams || static_cast<int>(threadIdx.x) >= spb * G) return;
+  const int g = static_cast<int>(threadIdx.x) % G;
+  const int c0 = g * VEC;
+  const int b = blockIdx.y;
+  const int w0 = e0 + stream * E;
+  const int n_e = min(E, e1 - w0);
+
+  // all token rows of the stream's blocks: block k covers tokens (w0 - 1 + k) M .. + M - 1
+  uint4 xr[NB][M], gr[NB][M];
+  const bf16_t* xb = x + static_cast<size_t>(b) * S * C + c0;
+  const bf16_t* gb = gate + static_cast<size_t>(b) * S * C + c0;
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int j = (w0 - 1 + k) * M + i;
+      const bool ok = j >= 0 && k <= n_e;
+      const size_t jr = static_cast<size_t>(ok ? j : 0) * C;
+      xr[k][i] = *reinterpret_cast<const uint4*>(xb + jr);
+      gr[k][i] = *reinterpret_cast<const uint4*>(gb + jr);
+    }
+  float bz[2 * M][VEC];  // slot biases, log2 domain
+#pragma unroll
+  for (int s2 = 0; s2 < 2 * M; ++s2) {
+    if (bias != nullptr) {
+      Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s2) * C + c0, bz[s2]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) bz[s2][i] *= kLog2e;
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) bz[s2][i] = 0.f;
+    }
+  }
+  auto unpack = [](const uint4& u, float (&v)[VEC]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  };
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e >= n_e) break;
+    const int w = w0 + e;
+    float out[VEC];
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch) out[ch] = 0.f;
+    // logits of the 2M slots (block e: slots 0..M-1, absent before token 0; block e+1: M..2M-1)
+    float a[2 * M][VEC];
+    float mx[VEC];
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch) mx[ch] = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < 2 * M; ++s2) {
+      float gv[VEC];
+      unpack(gr[e + s2 / M][s2 % M], gv);
+      const bool present = (w - 1) * M + s2 >= 0;
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) {
+        a[s2][ch] = present ? fmaf(gv[ch], kLog2e, bz[s2][ch]) : -INFINITY;
+        mx[ch] = fmaxf(mx[ch], a[s2][ch]);
+      }
+    }
+    float sum[VEC], acc[VEC];
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch) { sum[ch] = 0.f; acc[ch] = 0.f; }
+#pragma unroll
+    for (int s2 = 0; s2 < 2 * M; ++s2) {
+      float xv[VEC];
+      unpack(xr[e + s2 / M][s2 % M], xv);
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) {
+        const float p = __builtin_amdgcn_exp2f(a[s2][ch] - mx[ch]);  // 0 for absent slots
+        sum[ch] += p;
+        acc[ch] = fmaf(p, xv[ch], acc[ch]);
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch) out[ch] = acc[ch] * __builtin_amdgcn_rcpf(sum[ch]);
+    const double pos = static_cast<double>((static_cast<long long>(w) + 1) * M - 1 + pos_off);
+    rope_chunk<VEC, true>(out, c0, C, r, pos, inv_freq);
+    Chunk<bf16_t>::template store<VEC>(pool + (static_cast<size_t>(b) * N_cap + w) * C + c0, out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// compress, disjoint windows at a large rate (HCA, m = NG * GS slots, bf16, C = 512): one
+// workgroup per entry, NG wavefronts; wavefront p pools slots [p GS, (p + 1) GS) for all 512
+// channels (lane l owns channels 8l .. 8l + 7), in groups of 8 tokens whose loads (values,
+// gates, slot biases) are all issued before the group's arithmetic.  A group is pooled in two
+// passes (maximum, then exponentials) and merged into the wavefront's running state; the NG
+// states of a channel are merged through LDS by wavefront 0, which also applies RoPE.
+// ---------------------------------------------------------------------------
+template <int NG, int GS>
+__global__ void __launch_bounds__(NG * 64) compress_disjoint_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ gate, const float* __restrict__ bias,
+    bf16_t* __restrict__ pool, int S, int e0, int N_cap, int r, const RopeFreq rf, long long pos_off) {
+  constexpr int C = 512, VEC = 8, M = NG * GS, U = 8;
+  static_assert(GS % U == 0, "slot groups of 8");
+  __shared__ float red[NG][3][VEC][64];  // per wavefront: max, sum, acc of each lane's channels
+  __shared__ double inv_freq[kMaxRope / 2];
+  for (int i = threadIdx.x; i < r / 2; i += NG * 64) inv_freq[i] = rf.inv[i];
+  const int lane = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int b = blockIdx.y, w = e0 + blockIdx.x;
+  const int c0 = lane * VEC;
+  const bf16_t* xb = x + (static_cast<size_t>(b) * S + static_cast<size_t>(w) * M) * C + c0;
+  const bf16_t* gb = gate + (static_cast<size_t>(b) * S + static_cast<size_t>(w) * M) * C + c0;
+  float mx[VEC], sm[VEC], acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) { mx[i] = -INFINITY; sm[i] = 0.f; acc[i] = 0.f; }
+  auto unpack = [](const uint4& u, float (&v)[VEC]) {
+    const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  };
+#pragma unroll 1
+  for (int s0 = p * GS; s0 < (p + 1) * GS; s0 += U) {
+    uint4 xr[U], gr[U];
+    float bv[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      xr[u] = *reinterpret_cast<const uint4*>(xb + static_cast<size_t>(s0 + u) * C);
+      gr[u] = *reinterpret_cast<const uint4*>(gb + static_cast<size_t>(s0 + u) * C);
+      if (bias != nullptr) Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s0 + u) * C + c0, bv[u]);
+    }
+    float a[U][VEC], gm[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) gm[i] = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float gv[VEC];
+      unpack(gr[u], gv);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        a[u][i] = (bias != nullptr ? gv[i] + bv[u][i] : gv[i]) * kLog2e;
+        gm[i] = fmaxf(gm[i], a[u][i]);
+      }
+    }
+    // fold the group into the running state at the new maximum
+    float nm[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      nm[i] = fmaxf(mx[i], gm[i]);
+      const float f = __builtin_amdgcn_exp2f(mx[i] - nm[i]);  // 0 while the state is empty
+      sm[i] *= f;
+      acc[i] *= f;
+      mx[i] = nm[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float xv[VEC];
+      unpack(xr[u], xv);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float e = __builtin_amdgcn_exp2f(a[u][i] - nm[i]);
+        sm[i] += e;
+        acc[i] = fmaf(e, xv[i], acc[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    red[p][0][i][lane] = mx[i];
+    red[p][1][i][lane] = sm[i];
+    red[p][2][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (p != 0) return;
+  float out[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    float m_all = red[0][0][i][lane];
+#pragma unroll
+    for (int q = 1; q < NG; ++q) m_all = fmaxf(m_all, red[q][0][i][lane]);
+    float s_all = 0.f, a_all = 0.f;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const float f = __builtin_amdgcn_exp2f(red[q][0][i][lane] - m_all);
+      s_all = fmaf(red[q][1][i][lane], f, s_all);
+      a_all = fmaf(red[q][2][i][lane], f, a_all);
+    }
+    out[i] = a_all * __builtin_amdgcn_rcpf(s_all);
+  }
+  const double pos = static_cast<double>((static_cast<long long>(w) + 1) * M - 1 + pos_off);
+  rope_chunk<VEC, true>(out, c0, C, r, pos, inv_freq);
+  Chunk<bf16_t>::template store<VEC>(pool + (static_cast<size_t>(b) * N_cap + w) * C + c0, out);
+}
+
 hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, const void* gate_prev,
                            const float* bias, void* pool, int B, int S, int C, int m, int overlap, int e0,
                            int e1, int N_cap, int r, double theta, long long off, int dtype, hipStream_t st) {
   const bool v8 = (C % 8 == 0) && (C / 8 <= 256);
   if (!overlap) x_prev = gate_prev = nullptr;  // no earlier half
+  if (dtype == 1 && overlap && m == 4 && x_prev == nullptr && C % 8 == 0 && C / 8 <= 64 &&
+      64 % (C / 8) == 0 && e1 > e0) {
+    constexpr int E = 1;  // entries per stream (1: twice the wavefronts of 2, measured faster)
+    const int G = C / 8;
+    const int n_streams = static_cast<int>(div_up(static_cast<uint32_t>(e1 - e0), E));
+    const int nb = static_cast<int>(div_up(static_cast<uint32_t>(n_streams), 64 / G));
+    const int per = static_cast<int>(div_up(static_cast<uint32_t>(nb), 8));
+    hipLaunchKernelGGL((compress_window_kernel<4, E>), dim3(8 * per, B), dim3(64), 0, st,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gate), bias,
+                       static_cast<bf16_t*>(pool), S, C, e0, e1, N_cap, r, make_rope_freq(r, theta), off, G,
+                       n_streams, per);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && !overlap && m == 128 && C == 512 && e1 > e0) {
+    hipLaunchKernelGGL((compress_disjoint_kernel<8, 16>), dim3(e1 - e0, B), dim3(512), 0, st,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gate), bias,
+                       static_cast<bf16_t*>(pool), S, e0, N_cap, r, make_rope_freq(r, theta), off);
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     return v8 ? compress_t<bf16_t, 8>(x, gate, x_prev, gate_prev, bias, pool, B, S, C, m, overlap, e0, e1, N_cap, r,
                                       theta, off, st)
@@ -305,25 +542,33 @@ __global__ void __launch_bounds__(256) swa_kernel(const T* __restrict__ kv_raw, 
     __syncthreads();
   }
   const unsigned base = blk * blockDim.x * SWA_U + threadIdx.x;
+  // the chunks' rows, their sequences' start positions and their data are all requested
+  // before any store, so the stores wait for one round trip, not one per chunk
   float v[SWA_U][VEC];
+  unsigned rows[SWA_U];
+  int np0[SWA_U], kp0[SWA_U];
 #pragma unroll
   for (int u = 0; u < SWA_U; ++u) {
     const unsigned gid = base + u * blockDim.x;
     const unsigned ld = gid < total ? gid : total - 1;  // a valid chunk; unused past the end
     const unsigned row = ld / Gk;
+    rows[u] = row;
     const unsigned g = (rot ? Gn : 0) + (ld - row * Gk);
     Chunk<T>::template load<VEC>(kv_raw + (static_cast<size_t>(row) * G + g) * VEC, v[u]);
+    const unsigned b = row / static_cast<unsigned>(S_new);
+    np0[u] = new_pos0[b];
+    kp0[u] = kv_pos0[b];
   }
 #pragma unroll
   for (int u = 0; u < SWA_U; ++u) {
     const unsigned gid = base + u * blockDim.x;
     if (gid >= total) break;
-    const unsigned row = gid / Gk;  // b * S_new + i
+    const unsigned row = rows[u];  // b * S_new + i
     const int g = static_cast<int>((rot ? Gn : 0) + (gid - row * Gk));
     const int b = static_cast<int>(row / static_cast<unsigned>(S_new));
     const int i = static_cast<int>(row - static_cast<unsigned>(b) * S_new);
-    const long long seq = static_cast<long long>(new_pos0[b]) + i;
-    const long long dst = seq - kv_pos0[b];
+    const long long seq = static_cast<long long>(np0[u]) + i;
+    const long long dst = seq - kp0[u];
     if (dst < 0 || dst >= S_cap) continue;
     if (rot)
       rope_chunk<VEC, sizeof(T) == 2>(v[u], g * VEC, D, r, static_cast<double>(seq + pos_off),
