@@ -760,6 +760,12 @@ hipError_t launch_topk(const float* scores, const int* q_pos0, const int* n_pool
     if (N_cap <= 2048)
       hipLaunchKernelGGL((topk_wave<32>), grid, dim3(256), 0, st, scores, q_pos0, n_pool,
                          topk_idx, topk_score, rows, T, N_cap, m, k);
+    else if (N_cap <= 4096)
+      hipLaunchKernelGGL((topk_wave<64>), grid, dim3(256), 0, st, scores, q_pos0, n_pool,
+                         topk_idx, topk_score, rows, T, N_cap, m, k);
+    else if (N_cap <= 8192)  // rows of up to 8192 keys: one block of 256 threads, 32 keys a thread
+      hipLaunchKernelGGL((topk_radix<256, 32>), dim3(rows), dim3(256), 0, st, scores, q_pos0,
+                         n_pool, topk_idx, topk_score, T, N_cap, m, k);
     else  // strides past the 64 in registers are re-read from the score row on every pass
       hipLaunchKernelGGL((topk_wave<64>), grid, dim3(256), 0, st, scores, q_pos0, n_pool,
                          topk_idx, topk_score, rows, T, N_cap, m, k);

@@ -242,6 +242,14 @@ def test_index_topk_long_rows_ragged_visibility():
     _topk_case("bf16", 3, 1, 64, 128, 20000, 512, 4, [1199, 20399, 79999], [20000, 20000, 20000], 13)
 
 
+def test_index_topk_prefill_rows_4k_to_8k():
+    # many rows of 4097..8192 visible entries (the block-per-row selection with every key in
+    # registers): a near-full 8192-entry pool, and a second sequence whose rows hold ~4250
+    # entries with only 6 distinct scores (thousands of exact ties at the k-th slot)
+    _topk_case("bf16", 2, 40, 64, 128, 8192, 512, 4, [32700, 17000], [8192, 6000], 14,
+               few_rows=(1,))
+
+
 def test_index_topk_small_T_stream_path():
     # T = 3 queries per sequence on the streaming scorer (T < 8), ragged entry counts
     _topk_case("bf16", 2, 3, 64, 128, 3000, 300, 4, [7001, 4096], [1800, 3000], 12)
