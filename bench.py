@@ -704,7 +704,7 @@ def main():
         torch.cuda.empty_cache()
     att = kern["csa_attend"]
     src = kernel_hash("attend_mfma.hip", "common.h")
-    prof = load_profile("csa_attend", src)
+    prof = load_profile("csa_prefill/csa_attend", src)
     roof = {"kernel": "csa_attend", "bound": "mfma",
             "achieved": att["alg_flops"] / att["ms_mean"] / 1e9, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": att["alg_flops"] / att["ms_mean"] / 1e-3 / PEAK_BF16,
