@@ -741,6 +741,13 @@ def main():
         res["cpu_baseline"] = cpu_baseline()
     else:
         res["cpu_baseline"] = None
+    # release the device and host buffers before the line is printed, so the process exits
+    # promptly once it is read (bench.py starts no other process)
+    del clock, w
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

@@ -458,14 +458,17 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
     return;
   }
 
-  // keys of this thread: index j*NT + tid; 0 for indices >= V (discounted, never selected)
+  // keys of this thread: index j*NT + tid; 0 for indices >= V (discounted, never selected).
+  // All loads are issued before any is converted (indices clamped to the last key, in
+  // bounds): with the load and its use in one step, every key waited a memory round trip.
   const int n_strides = (V + NT - 1) / NT;
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = j * NT + tid;
-    key[j] = (j < n_strides && i < V) ? score_key(s[i]) : 0u;
-  }
+  for (int j = 0; j < KPT; ++j)
+    key[j] = j < n_strides ? __float_as_uint(s[min(j * NT + tid, V - 1)]) : 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    key[j] = (j < n_strides && j * NT + tid < V) ? score_key(__uint_as_float(key[j])) : 0u;
 
   // strides past the row are skipped (block-uniform); the last one may hold empty slots
   const int n_reg = min(n_strides, KPT);
@@ -649,12 +652,12 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
   }
 
   const int n_str = (V + 63) / 64;
-  uint32_t key[KPL];
+  uint32_t key[KPL];  // loads issued together (clamped in bounds), then converted
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int i = j * 64 + lane;
-    key[j] = (j < n_str && i < V) ? score_key(s[i]) : 0u;
-  }
+  for (int j = 0; j < KPL; ++j) key[j] = j < n_str ? __float_as_uint(s[min(j * 64 + lane, V - 1)]) : 0u;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j)
+    key[j] = (j < n_str && j * 64 + lane < V) ? score_key(__uint_as_float(key[j])) : 0u;
   const int n_reg = min(n_str, KPL);  // register strides in use (wave-uniform)
   const int n_inv = n_reg * 64 - min(V, n_reg * 64);
 

@@ -242,6 +242,14 @@ def test_index_topk_long_rows_ragged_visibility():
     _topk_case("bf16", 3, 1, 64, 128, 20000, 512, 4, [1199, 20399, 79999], [20000, 20000, 20000], 13)
 
 
+def test_index_topk_long_rows_other_scorers():
+    # few long rows (the block-per-row selection) scored by the other two scoring kernels:
+    # fp32 on the generic scorer (row 1 has 250 visible entries), and T = 16 on the MFMA
+    # scorer with exact ties at the k-th slot
+    _topk_case("fp32", 2, 1, 4, 32, 9000, 64, 4, [35999, 1000], [9000, 9000], 15)
+    _topk_case("bf16", 1, 16, 64, 128, 12000, 512, 4, [47980], [12000], 16, few_rows=(0,))
+
+
 def test_index_topk_prefill_rows_4k_to_8k():
     # many rows of 4097..8192 visible entries (the block-per-row selection with every key in
     # registers): a near-full 8192-entry pool, and a second sequence whose rows hold ~4250
