@@ -229,20 +229,18 @@ __global__ void __launch_bounds__(256, 2) index_score_mfma(
 // bytes in flight to cover HBM latency.  Lane (l32, half) loads 16 bytes of entry row l32 per
 // 16-dim step; the 8 steps of a sub-tile together read whole 256-byte rows.
 // ---------------------------------------------------------------------------
-template <int EPW>
-__global__ void __launch_bounds__(256) index_score_stream(
-    const bf16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const bf16_t* __restrict__ k_pool, const int* __restrict__ q_pos0,
-    const int* __restrict__ n_pool, float* __restrict__ scores, int T, int N_cap, int m) {
+// Scores of entries [e0, e1) of query (b, t) (e0 < e1 <= its visible count), streamed by one
+// wave: lane (l32, half) loads 16 bytes of entry row l32 per 16-dim step, the 8 steps of a
+// sub-tile together read whole 256-byte rows; three register sets rotate, so sub-tiles n0 + 32
+// and n0 + 64 are in flight while n0 is scored.
+__device__ __forceinline__ void stream_scores(const bf16_t* __restrict__ q_idx,
+                                              const float* __restrict__ w_idx,
+                                              const bf16_t* __restrict__ k_pool,
+                                              float* __restrict__ scores, int b, int t, int T,
+                                              int N_cap, int e0, int e1) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int t = blockIdx.y, b = blockIdx.z;
-  const int V = visible_entries(q_pos0, n_pool, b, t, m, N_cap);
-  const int e0 = (blockIdx.x * 4 + wave) * EPW;
-  if (e0 >= V) return;  // wave-uniform
-  const int e1 = min(V, e0 + EPW);
   const size_t qrow = static_cast<size_t>(b) * T + t;
 
   bf16x8_t qa[2][IX_CI / 16];
@@ -258,9 +256,7 @@ __global__ void __launch_bounds__(256) index_score_stream(
     for (int e = 0; e < 16; ++e) wv[hb][e] = wp[(e >> 2) * 8 + (e & 3)];
   }
 
-  // rows past e1 are clamped to e1 - 1 (a visible row): loads stay in bounds, results unused.
-  // Three register sets rotate: sub-tiles n0 + 32 and n0 + 64 are in flight while n0 is
-  // scored (two sub-tiles of prefetch per wave).
+  // rows past e1 are clamped to e1 - 1 (a visible row): loads stay in bounds, results unused
   const bf16_t* kb = k_pool + static_cast<size_t>(b) * N_cap * IX_CI + half * 8;
   float* srow = scores + qrow * N_cap;
   auto load = [&](uint4 (&dst)[IX_CI / 16], int n) {
@@ -300,6 +296,91 @@ __global__ void __launch_bounds__(256) index_score_stream(
     if (n0 + 32 < e1) score(b1, n0 + 32);
     if (n0 + 128 < e1) load(b1, n0 + 128);
     if (n0 + 64 < e1) score(b2, n0 + 64);
+  }
+}
+
+// Decode-sized T, many rows (index_score_stream): the scan is bound by reading the indexer keys
+// once (64 flops per byte), so every wave streams its own EPW consecutive entries of one query
+// straight from HBM into B-operand registers.  No LDS, no barriers.
+template <int EPW>
+__global__ void __launch_bounds__(256) index_score_stream(
+    const bf16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const bf16_t* __restrict__ k_pool, const int* __restrict__ q_pos0,
+    const int* __restrict__ n_pool, float* __restrict__ scores, int T, int N_cap, int m) {
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.y, b = blockIdx.z;
+  const int V = visible_entries(q_pos0, n_pool, b, t, m, N_cap);
+  const int e0 = (blockIdx.x * 4 + wave) * EPW;
+  if (e0 >= V) return;  // wave-uniform
+  stream_scores(q_idx, w_idx, k_pool, scores, b, t, T, N_cap, e0, min(V, e0 + EPW));
+}
+
+// Decode-sized T, up to kScanMaxRows rows (index_score_scan): a persistent grid whose waves
+// each take an equal share of all rows' 32-entry sub-tiles, as one contiguous range (part of a
+// row, or the end of one row and the start of the next).  A fixed number of entries per wave
+// would leave the device partly idle in the last round of waves; here every wave ends within
+// one sub-tile of the others.  Each block first forms the rows' sub-tile counts and their
+// prefix in LDS (thread tid owns rows RPT tid .. RPT tid + RPT - 1).
+constexpr int kScanMaxRows = 2048;
+__global__ void __launch_bounds__(256) index_score_scan(
+    const bf16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const bf16_t* __restrict__ k_pool, const int* __restrict__ q_pos0,
+    const int* __restrict__ n_pool, float* __restrict__ scores, int T, int N_cap, int m, int rows) {
+  constexpr int RPT = kScanMaxRows / 256;
+  __shared__ int pre[kScanMaxRows + 1];  // sub-tiles of the rows before row r
+  __shared__ int wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cnt[RPT];
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = tid * RPT + j;
+    cnt[j] = r < rows ? (visible_entries(q_pos0, n_pool, r / T, r % T, m, N_cap) + 31) / 32 : 0;
+    mine += cnt[j];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int run = incl - mine, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    run += w < wave ? wtot[w] : 0;
+    total += wtot[w];
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = tid * RPT + j;
+    if (r < rows) pre[r] = run;
+    run += cnt[j];
+  }
+  if (tid == 0) pre[rows] = total;
+  __syncthreads();
+
+  const long long W = static_cast<long long>(gridDim.x) * 4;
+  const long long wid = static_cast<long long>(blockIdx.x) * 4 + wave;
+  int s = static_cast<int>(total * wid / W);
+  const int s1 = static_cast<int>(total * (wid + 1) / W);
+  if (s >= s1) return;  // wave-uniform
+  // the row holding sub-tile s: the last r with pre[r] <= s
+  int r = 0, hi = rows - 1;
+  while (r < hi) {
+    const int mid = (r + hi + 1) >> 1;
+    if (pre[mid] <= s) r = mid;
+    else hi = mid - 1;
+  }
+  while (s < s1) {
+    while (pre[r + 1] <= s) ++r;  // rows without entries
+    const int end = min(s1, pre[r + 1]);
+    const int b = r / T, t = r % T;
+    const int V = visible_entries(q_pos0, n_pool, b, t, m, N_cap);
+    stream_scores(q_idx, w_idx, k_pool, scores, b, t, T, N_cap, (s - pre[r]) * 32,
+                  min(V, (end - pre[r]) * 32));
+    s = end;
   }
 }
 
@@ -345,8 +426,21 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
       dim3 grid(div_up(T, NWV), 1, B);
       hipLaunchKernelGGL((index_score_mfma<NWV>), grid, dim3(NWV * 64), 0, st, qp, w_idx, kp,
                          q_pos0, n_pool, scores, T, N_cap, m);
+    } else if (B * T <= kScanMaxRows) {
+      // decode-sized T: a persistent grid (two blocks of four waves per CU) over every row
+      static int n_cu = 0;
+      if (n_cu == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+          n_cu = n;
+        else
+          return hipErrorInvalidDevice;
+      }
+      hipLaunchKernelGGL(index_score_scan, dim3(2 * n_cu), dim3(256), 0, st, qp, w_idx, kp, q_pos0,
+                         n_pool, scores, T, N_cap, m, B * T);
     } else {
-      // decode-sized T: one query per block row, 4 waves x EPW entries per block
+      // decode-sized T, many rows: one query per block row, 4 waves x EPW entries per block
       constexpr int EPW = 256;
       dim3 grid(div_up(N_cap, 4 * EPW), T, B);
       hipLaunchKernelGGL((index_score_stream<EPW>), grid, dim3(256), 0, st, qp, w_idx, kp, q_pos0,
