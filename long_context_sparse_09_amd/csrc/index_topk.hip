@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(256) index_score_stream(
 // row, or the end of one row and the start of the next).  A fixed number of entries per wave
 // would leave the device partly idle in the last round of waves; here every wave ends within
 // one sub-tile of the others.  Each block first forms the rows' sub-tile counts and their
-// prefix in LDS (thread tid owns rows RPT tid .. RPT tid + RPT - 1).
+// prefix in LDS.
 constexpr int kScanMaxRows = 2048;
 __global__ void __launch_bounds__(256) index_score_scan(
     const bf16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
@@ -330,12 +330,24 @@ __global__ void __launch_bounds__(256) index_score_scan(
   __shared__ int pre[kScanMaxRows + 1];  // sub-tiles of the rows before row r
   __shared__ int wtot[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // thread tid owns rows rpt*tid .. rpt*tid + rpt - 1 (one row each up to 256 rows); every
+  // position load is issued before any count is formed (one memory round trip, not one per row)
+  const int rpt = (rows + 255) / 256;
+  int qp[RPT], np[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int b = min(tid * rpt + j, rows - 1) / T;
+    qp[j] = q_pos0[b];
+    np[j] = n_pool[b];
+  }
   int cnt[RPT];
   int mine = 0;
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
-    const int r = tid * RPT + j;
-    cnt[j] = r < rows ? (visible_entries(q_pos0, n_pool, r / T, r % T, m, N_cap) + 31) / 32 : 0;
+    const int r = tid * rpt + j;
+    long long v = (static_cast<long long>(qp[j]) + r % T + 1) / m;  // visible_entries, inlined
+    v = min(min(v, static_cast<long long>(np[j])), static_cast<long long>(N_cap));
+    cnt[j] = (j < rpt && r < rows) ? (static_cast<int>(max(v, 0LL)) + 31) / 32 : 0;
     mine += cnt[j];
   }
   int incl = mine;
@@ -354,8 +366,8 @@ __global__ void __launch_bounds__(256) index_score_scan(
   }
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
-    const int r = tid * RPT + j;
-    if (r < rows) pre[r] = run;
+    const int r = tid * rpt + j;
+    if (j < rpt && r < rows) pre[r] = run;
     run += cnt[j];
   }
   if (tid == 0) pre[rows] = total;
