@@ -197,17 +197,22 @@ __global__ void __launch_bounds__(64) compress_window_kernel(
       xr[k][i] = *reinterpret_cast<const uint4*>(xb + jr);
       gr[k][i] = *reinterpret_cast<const uint4*>(gb + jr);
     }
-  float bz[2 * M][VEC];  // slot biases, log2 domain
+  // slot biases, log2 domain: every slot's loads are issued before any is scaled (scaling each
+  // slot as it arrives made every later slot's loads wait a memory round trip)
+  float bz[2 * M][VEC];
+  if (bias != nullptr) {
 #pragma unroll
-  for (int s2 = 0; s2 < 2 * M; ++s2) {
-    if (bias != nullptr) {
+    for (int s2 = 0; s2 < 2 * M; ++s2)
       Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s2) * C + c0, bz[s2]);
 #pragma unroll
+    for (int s2 = 0; s2 < 2 * M; ++s2)
+#pragma unroll
       for (int i = 0; i < VEC; ++i) bz[s2][i] *= kLog2e;
-    } else {
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < 2 * M; ++s2)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) bz[s2][i] = 0.f;
-    }
   }
   auto unpack = [](const uint4& u, float (&v)[VEC]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
