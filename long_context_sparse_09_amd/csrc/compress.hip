@@ -439,46 +439,61 @@ __global__ void __launch_bounds__(256) cache_update_kernel(
   const int lo = overlap ? (w - 1) * m : w * m;
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     const int c0 = g * VEC;
-    float v[VEC];
-    Chunk<T>::template load<VEC>(x_new + static_cast<size_t>(b) * C + c0, v);
-    Chunk<T>::template store<VEC>(x_ring + (ring0 + slot) * C + c0, v);
-    Chunk<T>::template load<VEC>(g_new + static_cast<size_t>(b) * C + c0, v);
-    Chunk<T>::template store<VEC>(g_ring + (ring0 + slot) * C + c0, v);
-    if (xp_ring != nullptr) {  // the second projection, for the windows this token starts
-      Chunk<T>::template load<VEC>(xp_new + static_cast<size_t>(b) * C + c0, v);
-      Chunk<T>::template store<VEC>(xp_ring + (ring0 + slot) * C + c0, v);
-      Chunk<T>::template load<VEC>(gp_new + static_cast<size_t>(b) * C + c0, v);
-      Chunk<T>::template store<VEC>(gp_ring + (ring0 + slot) * C + c0, v);
+    // the new token's rows: every load before any store (each load waited for in turn cost a
+    // memory round trip per row)
+    const bool two = xp_ring != nullptr;  // the second projection, for the windows this token starts
+    float v0[VEC], v1[VEC], v2[VEC], v3[VEC];
+    Chunk<T>::template load<VEC>(x_new + static_cast<size_t>(b) * C + c0, v0);
+    Chunk<T>::template load<VEC>(g_new + static_cast<size_t>(b) * C + c0, v1);
+    Chunk<T>::template load<VEC>((two ? xp_new : x_new) + static_cast<size_t>(b) * C + c0, v2);
+    Chunk<T>::template load<VEC>((two ? gp_new : g_new) + static_cast<size_t>(b) * C + c0, v3);
+    Chunk<T>::template store<VEC>(x_ring + (ring0 + slot) * C + c0, v0);
+    Chunk<T>::template store<VEC>(g_ring + (ring0 + slot) * C + c0, v1);
+    if (two) {
+      Chunk<T>::template store<VEC>(xp_ring + (ring0 + slot) * C + c0, v2);
+      Chunk<T>::template store<VEC>(gp_ring + (ring0 + slot) * C + c0, v3);
     }
     if (!closes) continue;
     float mx[VEC], sm[VEC], acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) { mx[i] = -INFINITY; sm[i] = 0.f; acc[i] = 0.f; }
-    for (int s = 0; s < span; ++s) {
-      const int p = lo + s;  // token position; absent before 0
-      if (p < 0) continue;
-      const size_t row = ring0 + p % span;
-      float xv[VEC], gv[VEC];
-      const bool early = xp_ring != nullptr && s < m;  // the earlier half's second projection
-      Chunk<T>::template load<VEC>((early ? xp_ring : x_ring) + row * C + c0, xv);
-      Chunk<T>::template load<VEC>((early ? gp_ring : g_ring) + row * C + c0, gv);
-      if (bias != nullptr) {
-        float bv[VEC];
-        Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s) * C + c0, bv);
+    // slots in batches of SB: a batch's loads are all issued, then its slots are folded into
+    // the online softmax in slot order (the order compress_kernel uses)
+    constexpr int SB = 4;
+    for (int s0 = 0; s0 < span; s0 += SB) {
+      float xv[SB][VEC], gv[SB][VEC], bv[SB][VEC];
+      // loads are unconditional (slots past the span or before position 0 read a clamped,
+      // valid row and are skipped below): a load under a branch is waited for inside it
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) gv[i] += bv[i];
+      for (int j = 0; j < SB; ++j) {
+        const int s = min(s0 + j, span - 1);
+        const int p = max(lo + s, 0);  // token position; absent before 0
+        const size_t row = ring0 + p % span;
+        const bool early = two && s < m;  // the earlier half's second projection
+        Chunk<T>::template load<VEC>((early ? xp_ring : x_ring) + row * C + c0, xv[j]);
+        Chunk<T>::template load<VEC>((early ? gp_ring : g_ring) + row * C + c0, gv[j]);
+      }
+      if (bias != nullptr) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+          Chunk<float>::template load<VEC>(bias + static_cast<size_t>(min(s0 + j, span - 1)) * C + c0, bv[j]);
       }
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const float a = gv[i] * kLog2e;
-        const float d = exp2f(-fabsf(a - mx[i]));
-        if (a > mx[i]) {
-          sm[i] = sm[i] * d + 1.f;
-          acc[i] = acc[i] * d + xv[i];
-          mx[i] = a;
-        } else {
-          sm[i] += d;
-          acc[i] += d * xv[i];
+      for (int j = 0; j < SB; ++j) {
+        const int s = s0 + j;
+        if (s >= span || lo + s < 0) continue;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float a = (bias != nullptr ? gv[j][i] + bv[j][i] : gv[j][i]) * kLog2e;
+          const float d = exp2f(-fabsf(a - mx[i]));
+          if (a > mx[i]) {
+            sm[i] = sm[i] * d + 1.f;
+            acc[i] = acc[i] * d + xv[j][i];
+            mx[i] = a;
+          } else {
+            sm[i] += d;
+            acc[i] += d * xv[j][i];
+          }
         }
       }
     }
