@@ -152,7 +152,7 @@ int compressor_cache_update_split(const void* x_new, const void* gate_new, const
  * Reading R9: the min(k, V) largest scores are kept; equal scores keep the lower entry
  * index; -0.0 ranks as +0.0.  topk_idx[b,t,:] lists the kept entries in ascending index
  * order, then -1 in the remaining slots; topk_score (optional) holds their scores (and 0
- * beside each -1).
+ * beside each -1; a kept score of -0.0 may be reported as +0.0).
  *
  *   q_idx   : [B, T, nI, cI] dtype.  w_idx : [B, T, nI] float32.
  *   k_pool  : [B, N_cap, cI] dtype (the indexer's own compressed keys, not rotated).

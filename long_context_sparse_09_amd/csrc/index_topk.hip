@@ -479,12 +479,12 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
 // owns indices j*NT + tid; the first KPT of them stay in registers, later ones are re-read
 // (coalesced) from the score row on every pass.
 //
-// Threshold: radix select over 8 passes of 4-bit digits, most significant first.  Each
-// lane counts into its own column of a per-wave [16 digits][64 lanes] LDS histogram, so the
-// increments never collide whatever the score distribution (a shared 256-bin histogram
+// Threshold: radix select over 8 passes of 4-bit digits, most significant first.  Lane l of
+// every wave counts into column l of a [16 digits][64 lanes] LDS histogram, so the lanes of
+// one atomic instruction never collide whatever the score distribution (a 256-bin histogram
 // serialises when most keys share a digit, as the top byte of similar-magnitude floats
-// does).  The pass stops early once the chosen digit's bucket holds exactly the keys still
-// needed.
+// does).  Wave d sums digit d's column with DPP moves.  The pass stops early once the chosen
+// digit's bucket holds exactly the keys still needed.
 //
 // Output: index-ordered compaction through LDS bitmaps, segment by segment (32768 indices):
 // one bit per key above the threshold and one per key equal to it (both from wave ballots),
@@ -499,23 +499,39 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return max(u, 1u);  // 0 marks "no key" (only one negative NaN pattern is moved, to 1)
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+// Histogram row of a key in a radix pass: its digit at `shift` when the key carries the
+// digits chosen so far (prefix; its bits at and below the digit are 0), else row 16, which
+// nobody reads.  (key ^ prefix) >> shift keeps set bits above the digit exactly for keys
+// outside the prefix.
+__device__ __forceinline__ uint32_t digit_row(uint32_t key, uint32_t prefix, int shift) {
+  return min((key ^ prefix) >> shift, 16u);
+}
+
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS round trips): a
+// Hillis-Steele scan inside each row of 16 lanes (source lanes outside the row read 0), then
+// rows 1 and 3 add the last lane of the row before and rows 2 and 3 the last lane of row 1.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 
-// Block-wide exclusive prefix sum of v over threads in tid order; *total = block sum.
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
+
+// Block-wide exclusive prefix sum of v over threads in tid order; *total = block sum.  One
+// barrier: a caller alternates between two wsum buffers, so that a buffer is rewritten only
+// after a later scan's barrier, by which time every thread has read it.
 template <int NT>
 __device__ __forceinline__ int block_scan_excl(int v, int* total, int* wsum) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(incl, off);
-    if (lane >= off) incl += u;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int before = 0, all = 0;
@@ -525,7 +541,6 @@ __device__ __forceinline__ int block_scan_excl(int v, int* total, int* wsum) {
     before += (w < wave) ? c : 0;
     all += c;
   }
-  __syncthreads();  // wsum reusable
   *total = all;
   return before + incl - v;
 }
@@ -543,10 +558,10 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
   constexpr int NW = NT / 64;
   static_assert(kSegIdx % NT == 0 && NT % 64 == 0, "segment = whole block strides");
   static_assert(KPT * NT <= kSegIdx, "register keys must fit the first segment");
-  __shared__ uint32_t hist[NW][16][64];
+  __shared__ uint32_t hist[17][64];  // [digit][lane], shared by the block's waves; row 16 unread
   __shared__ uint32_t gtbits[kSegWords], eqbits[kSegWords];
-  __shared__ int tot[16];
-  __shared__ int wsum[NW];
+  __shared__ __attribute__((aligned(16))) int tot[16];
+  __shared__ int wsum[2][NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qrow = blockIdx.x;
   const int b = qrow / T, t = qrow % T;
@@ -579,45 +594,46 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
   // strides past the row are skipped (block-uniform); the last one may hold empty slots
   const int n_reg = min(n_strides, KPT);
   const int n_inv = n_reg * NT - min(V, n_reg * NT);
-  for (int i = tid; i < NW * 16 * 64; i += NT) (&hist[0][0][0])[i] = 0;
+  for (int i = tid; i < 16 * 64; i += NT) (&hist[0][0])[i] = 0;  // row 16 is never read
   __syncthreads();
 
   uint32_t prefix = 0, mask = 0;
   int remaining = kk;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 28 - 4 * pass;
-    uint32_t* hcol = &hist[wave][0][lane];
-    // branch-free: a key outside the prefix adds 0
+    uint32_t* hcol = &hist[0][lane];
+    // branch-free: a key outside the prefix counts in row 16
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (j < n_reg)
-        atomicAdd(hcol + ((key[j] >> shift) & 15u) * 64,
-                  static_cast<uint32_t>((key[j] & mask) == prefix));
+      if (j < n_reg) atomicAdd(hcol + digit_row(key[j], prefix, shift) * 64, 1u);
     for (int j = KPT; j < n_strides; ++j) {
       const int i = j * NT + tid;
       if (i >= V) break;
-      const uint32_t kj = score_key(s[i]);
-      atomicAdd(hcol + ((kj >> shift) & 15u) * 64, static_cast<uint32_t>((kj & mask) == prefix));
+      atomicAdd(hcol + digit_row(score_key(s[i]), prefix, shift) * 64, 1u);
     }
     __syncthreads();
-    for (int d = wave; d < 16; d += NW) {
-      int c = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        c += static_cast<int>(hist[w][d][lane]);
-        hist[w][d][lane] = 0;
-      }
-      c = wave_sum(c);
+    for (int d = wave; d < 16; d += NW) {
+      const int c = wave_sum(static_cast<int>(hist[d][lane]));
+      hist[d][lane] = 0;
       // the n_inv empty register slots hold key 0: digit 0 while the prefix is all zeros
       if (lane == 0) tot[d] = c - ((d == 0 && prefix == 0u) ? n_inv : 0);
     }
     __syncthreads();
-    // every thread derives the digit from the 16 totals (no third barrier)
+    // every thread derives the digit from the 16 totals (no third barrier), read at once
+    int tv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int4 x = reinterpret_cast<const int4*>(tot)[q];
+      tv[4 * q] = x.x; tv[4 * q + 1] = x.y; tv[4 * q + 2] = x.z; tv[4 * q + 3] = x.w;
+    }
     int above = 0, digit = 0, in_digit = 0;
+    bool found = false;
+#pragma unroll
     for (int d = 15; d >= 0; --d) {
-      const int c = tot[d];
-      if (above + c >= remaining) { digit = d; in_digit = c; break; }
-      above += c;
+      const int c = tv[d];
+      if (!found && above + c >= remaining) { digit = d; in_digit = c; found = true; }
+      if (!found) above += c;
     }
     remaining -= above;
     prefix |= static_cast<uint32_t>(digit) << shift;
@@ -665,7 +681,7 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
     for (int q = 0; q < WPT; ++q)
       if (w0 + q < n_words) eq_cnt += __popc(eqbits[w0 + q]);
     int eq_tot;
-    int eq_pre = eq_base + block_scan_excl<NT>(eq_cnt, &eq_tot, wsum);
+    int eq_pre = eq_base + block_scan_excl<NT>(eq_cnt, &eq_tot, wsum[0]);
     uint32_t sel[WPT];
     int sel_cnt = 0;
 #pragma unroll
@@ -686,7 +702,7 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
       }
     }
     int sel_tot;
-    int pos = out_base + block_scan_excl<NT>(sel_cnt, &sel_tot, wsum);
+    int pos = out_base + block_scan_excl<NT>(sel_cnt, &sel_tot, wsum[1]);
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
       uint32_t w = sel[q];
@@ -703,7 +719,8 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
     }
     eq_base += eq_tot;
     out_base += sel_tot;
-    // block_scan_excl ends with a barrier: the bitmaps may be rebuilt for the next segment
+    // every bitmap read came before the barrier of the second scan: the next segment may
+    // rebuild them
   }
   for (int p = kk + tid; p < k; p += NT) {
     out_i[p] = -1;
@@ -724,6 +741,11 @@ __device__ __forceinline__ void lds_wave_sync() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// The score a key encodes (inverse of score_key; a score of -0.0 comes back as +0.0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ int quad_sum(int x) {
   x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
   x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
@@ -737,7 +759,7 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
                                                  int* __restrict__ topk_idx,
                                                  float* __restrict__ topk_score, int rows, int T,
                                                  int N_cap, int m, int k) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[4][16][64];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][17][64];  // row 16 unread
   __shared__ __attribute__((aligned(16))) int tots[4][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
@@ -780,15 +802,10 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
     const int shift = 28 - 4 * pass;
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
-      if (j < n_reg)
-        atomicAdd(hc + ((key[j] >> shift) & 15u) * 64,
-                  static_cast<uint32_t>((key[j] & mask) == prefix));
+      if (j < n_reg) atomicAdd(hc + digit_row(key[j], prefix, shift) * 64, 1u);
     for (int j = KPL; j < n_str; ++j) {
       const int i = j * 64 + lane;
-      if (i < V) {
-        const uint32_t kj = score_key(s[i]);
-        atomicAdd(hc + ((kj >> shift) & 15u) * 64, static_cast<uint32_t>((kj & mask) == prefix));
-      }
+      if (i < V) atomicAdd(hc + digit_row(score_key(s[i]), prefix, shift) * 64, 1u);
     }
     lds_wave_sync();
     int c = 0;
@@ -838,7 +855,7 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
     const int pos = out_pos + __popcll(sb & below);
     if (sel && pos < k) {  // exactly kk keys are selected; the bound only guards the buffer
       out_i[pos] = i;
-      if (out_s) out_s[pos] = s[i];
+      if (out_s) out_s[pos] = key_score(kj);  // from the key: no reload of the row
     }
     out_pos += __popcll(sb);
   };
