@@ -70,18 +70,35 @@ class DecodeCache:
         aw = attend_workspace_size(B, 1, sh.H, D)
         self.att_ws = torch.empty(aw, dtype=torch.uint8, device=dev) if aw > 0 else None
         self.out = torch.empty(B, 1, sh.H, D, dtype=sh.dtype, device=dev)
+        # pinned staging buffers for the per-step integers, and their last copies' events
+        self._stage = [torch.empty(4, B, dtype=torch.int32, pin_memory=True) for _ in range(4)]
+        self._stage_ev = [torch.cuda.Event() for _ in range(4)]
+        self._stage_i = 0
 
     # ------------------------------------------------------------------ positions
     def _kv_pos0(self):
         return self.L - self.sh.W - self.s
 
+    def _h2d(self, dst: torch.Tensor, host: np.ndarray) -> None:
+        """dst (device int32) <- host, ordered on the current stream and asynchronous to the
+        host: through one of four pinned staging buffers, each rewritten only after the copy
+        that last read it has run.  (A copy from pageable memory makes the host wait for the
+        device, and the device then idles while the host issues the step's launches.)"""
+        i = self._stage_i
+        self._stage_i = (i + 1) % len(self._stage)
+        self._stage_ev[i].synchronize()
+        buf = self._stage[i][: host.shape[0]]
+        buf.copy_(torch.from_numpy(host))
+        dst.copy_(buf, non_blocking=True)
+        self._stage_ev[i].record()
+
     def _upload(self):
-        """Copy this step's per-sequence integers to the device (synchronous, current stream)."""
+        """Copy this step's per-sequence integers to the device (current stream)."""
         sh = self.sh
         rate = {"csa": sh.m, "hca": sh.m_hca}.get(self.kind, 1)
         host = np.stack([self.L, self.L - 1, self._kv_pos0(),
                          np.minimum(self.L // rate, self.n_cap)]).astype(np.int32)
-        self.meta.copy_(torch.from_numpy(host))
+        self._h2d(self.meta, host)
         self.lengths_d, self.q_pos0_d, self.kv_pos0_d, self.n_pool_d = self.meta.unbind(0)
 
     # ------------------------------------------------------------------ prefill
@@ -133,7 +150,7 @@ class DecodeCache:
         sh, p = self.sh, self.params
         if self.s == self.G:  # refill: the live W rows move to the front of the other buffer
             old = self._kv_pos0()
-            self.refill_meta.copy_(torch.from_numpy(np.stack([old + self.s, old]).astype(np.int32)))
+            self._h2d(self.refill_meta, np.stack([old + self.s, old]).astype(np.int32))
             swa_concat(self.win[self.cur], self.win[1 - self.cur], self.refill_meta[0],
                        self.refill_meta[1], 0, 10000.0)
             self.cur = 1 - self.cur
