@@ -479,12 +479,17 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
 // owns indices j*NT + tid; the first KPT of them stay in registers, later ones are re-read
 // (coalesced) from the score row on every pass.
 //
-// Threshold: radix select over 8 passes of 4-bit digits, most significant first.  Lane l of
-// every wave counts into column l of a [16 digits][64 lanes] LDS histogram, so the lanes of
-// one atomic instruction never collide whatever the score distribution (a 256-bin histogram
-// serialises when most keys share a digit, as the top byte of similar-magnitude floats
-// does).  Wave d sums digit d's column with DPP moves.  The pass stops early once the chosen
-// digit's bucket holds exactly the keys still needed.
+// Threshold: radix select, most significant digit first.  The first digit (4 bits) is
+// counted by every key: lane l of every wave counts into column l of a [16 digits][64
+// lanes] LDS histogram, so the lanes of one atomic never collide whatever the score
+// distribution, and wave d sums digit d's column with DPP moves.  The digits of 11, 11 and
+// 6 bits after it are counted only by the keys that carry the digits chosen so far, in a
+// 2048-bin histogram (a key outside them adds to a lane-private spare bin); a block scan of
+// the threads' bin sums (thread t holds 2048/NT bins, the highest first) finds the wave, a
+// wave scan the thread and a walk of its bins the digit.  A pass stops the search once the
+// chosen bin holds exactly the keys still needed: on continuous scores after three passes,
+// against five to seven of 4-bit digits.  Two histograms alternate, so one is cleared while
+// the other is read; two barriers per pass.
 //
 // Output: index-ordered compaction through LDS bitmaps, segment by segment (32768 indices):
 // one bit per key above the threshold and one per key equal to it (both from wave ballots),
@@ -499,12 +504,22 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return max(u, 1u);  // 0 marks "no key" (only one negative NaN pattern is moved, to 1)
 }
 
-// Histogram row of a key in a radix pass: its digit at `shift` when the key carries the
-// digits chosen so far (prefix; its bits at and below the digit are 0), else row 16, which
+// Radix schedule of the selection, most significant digit first: a 4-bit digit (bits
+// 31..28) counted on lane-private LDS columns, where every key takes part and same-digit
+// keys must not pile onto one address, then digits of 11, 11 and 6 bits counted in a
+// 2048-bin histogram, where only the keys still in play are spread over the bins.
+constexpr int kBins = 2048;
+__device__ __forceinline__ int radix_shift(int pass) { return pass == 1 ? 17 : (pass == 2 ? 6 : 0); }
+__device__ __forceinline__ int radix_width(int pass) { return pass == 3 ? 6 : 11; }
+
+// Histogram bin of a key in a radix pass: its digit at `shift` when the key carries the
+// digits chosen so far (prefix; its bits at and below the digit are 0), else `spare`, a bin
 // nobody reads.  (key ^ prefix) >> shift keeps set bits above the digit exactly for keys
 // outside the prefix.
-__device__ __forceinline__ uint32_t digit_row(uint32_t key, uint32_t prefix, int shift) {
-  return min((key ^ prefix) >> shift, 16u);
+__device__ __forceinline__ uint32_t radix_bin(uint32_t key, uint32_t prefix, int shift, int width,
+                                              uint32_t spare) {
+  const uint32_t u = (key ^ prefix) >> shift;
+  return u < (1u << width) ? u : spare;
 }
 
 // Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS round trips): a
@@ -558,8 +573,10 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
   constexpr int NW = NT / 64;
   static_assert(kSegIdx % NT == 0 && NT % 64 == 0, "segment = whole block strides");
   static_assert(KPT * NT <= kSegIdx, "register keys must fit the first segment");
-  __shared__ uint32_t hist[17][64];  // [digit][lane], shared by the block's waves; row 16 unread
+  // two histograms used in alternate passes: kBins digit bins, then one spare bin per lane
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins + 64];
   __shared__ uint32_t gtbits[kSegWords], eqbits[kSegWords];
+  __shared__ __attribute__((aligned(16))) int wtot[NW];
   __shared__ __attribute__((aligned(16))) int tot[16];
   __shared__ int wsum[2][NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -594,34 +611,36 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
   // strides past the row are skipped (block-uniform); the last one may hold empty slots
   const int n_reg = min(n_strides, KPT);
   const int n_inv = n_reg * NT - min(V, n_reg * NT);
-  for (int i = tid; i < 16 * 64; i += NT) (&hist[0][0])[i] = 0;  // row 16 is never read
+  for (int i = tid; i < 2 * (kBins + 64); i += NT) (&hist[0][0])[i] = 0;
   __syncthreads();
 
+  // Thread t owns the BPT bins kBins - BPT(t+1) .. kBins - BPT t - 1: in thread order the
+  // bins run from the highest digit down, so a block scan of the threads' bin sums gives
+  // the count of keys at or above each thread's bins.
+  constexpr int BPT = kBins / NT;
+  static_assert(BPT * NT == kBins && BPT <= 8, "bins per thread");
   uint32_t prefix = 0, mask = 0;
   int remaining = kk;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 28 - 4 * pass;
+  bool done = false;
+  {  // first digit: bits 31..28 on lane-private columns, [digit][lane] in hist[0]
     uint32_t* hcol = &hist[0][lane];
-    // branch-free: a key outside the prefix counts in row 16
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (j < n_reg) atomicAdd(hcol + digit_row(key[j], prefix, shift) * 64, 1u);
+      if (j < n_reg) atomicAdd(hcol + (key[j] >> 28) * 64, 1u);
     for (int j = KPT; j < n_strides; ++j) {
       const int i = j * NT + tid;
       if (i >= V) break;
-      atomicAdd(hcol + digit_row(score_key(s[i]), prefix, shift) * 64, 1u);
+      atomicAdd(hcol + (score_key(s[i]) >> 28) * 64, 1u);
     }
     __syncthreads();
 #pragma unroll
     for (int d = wave; d < 16; d += NW) {
-      const int c = wave_sum(static_cast<int>(hist[d][lane]));
-      hist[d][lane] = 0;
-      // the n_inv empty register slots hold key 0: digit 0 while the prefix is all zeros
-      if (lane == 0) tot[d] = c - ((d == 0 && prefix == 0u) ? n_inv : 0);
+      const int c = wave_sum(static_cast<int>(hist[0][d * 64 + lane]));
+      // the n_inv empty register slots hold key 0: digit 0
+      if (lane == 0) tot[d] = c - (d == 0 ? n_inv : 0);
     }
     __syncthreads();
-    // every thread derives the digit from the 16 totals (no third barrier), read at once
-    int tv[16];
+    int tv[16];  // every thread derives the digit from the 16 totals, read at once
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int4 x = reinterpret_cast<const int4*>(tot)[q];
@@ -636,9 +655,74 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
       if (!found) above += c;
     }
     remaining -= above;
+    prefix = static_cast<uint32_t>(digit) << 28;
+    mask = 0xF0000000u;
+    done = in_digit == remaining;
+  }
+  // passes 1..3 in hist[1], hist[0], hist[1]: hist[0]'s columns are cleared in pass 1
+#pragma unroll 1
+  for (int pass = 1; pass < 4 && !done; ++pass) {
+    const int shift = radix_shift(pass), width = radix_width(pass);
+    uint32_t* h = hist[pass & 1];
+    const uint32_t spare = kBins + lane;  // keys outside the prefix: a lane-private bin
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (j < n_reg) atomicAdd(h + radix_bin(key[j], prefix, shift, width, spare), 1u);
+    for (int j = KPT; j < n_strides; ++j) {
+      const int i = j * NT + tid;
+      if (i >= V) break;
+      atomicAdd(h + radix_bin(score_key(s[i]), prefix, shift, width, spare), 1u);
+    }
+    __syncthreads();
+    // this thread's bins (and the other histogram's, cleared for the next pass: its last
+    // readers finished before the barrier above, its next writers come after the next)
+    const int b0 = kBins - BPT * (tid + 1);
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      mine += static_cast<int>(h[b0 + i]);
+      hist[(pass + 1) & 1][b0 + i] = 0;
+    }
+    // the n_inv empty register slots hold key 0: bin 0 while the prefix is all zeros
+    if (b0 == 0 && prefix == 0u) mine -= n_inv;
+    const int incl = wave_incl_scan(mine);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    // the wave whose bins hold the remaining-th key from the top, then (every wave alike)
+    // the thread within it and the bin within that thread
+    int above = 0, ws = 0;
+    bool found = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = wtot[w];
+      if (!found && above + c >= remaining) { ws = w; found = true; }
+      if (!found) above += c;
+    }
+    const int bw = kBins - BPT * (64 * ws + lane + 1);  // the bins of thread 64 ws + lane
+    int v[BPT], lsum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      v[i] = static_cast<int>(h[bw + i]);
+      if (bw + i == 0 && prefix == 0u) v[i] -= n_inv;
+      lsum += v[i];
+    }
+    const int lincl = wave_incl_scan(lsum);
+    const unsigned long long hit = __ballot(above + lincl >= remaining);
+    const int L = __builtin_ctzll(hit);
+    above += __builtin_amdgcn_readlane(lincl - lsum, L);
+    int digit = 0, in_digit = 0;
+    found = false;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {  // the lane's bins from the highest down
+      const int c = __builtin_amdgcn_readlane(v[i], L);
+      if (!found && above + c >= remaining) { digit = bw + i; in_digit = c; found = true; }
+      if (!found) above += c;
+    }
+    digit = __builtin_amdgcn_readlane(digit, L);  // bw differs per lane: take lane L's
+    remaining -= above;
     prefix |= static_cast<uint32_t>(digit) << shift;
-    mask |= 15u << shift;
-    if (in_digit == remaining) break;  // the whole bucket is taken: threshold found
+    mask |= ((1u << width) - 1u) << shift;
+    done = in_digit == remaining;  // the whole bucket is taken: threshold found
   }
 
   // index-ordered compaction; equal keys (under mask) taken lowest index first
@@ -730,10 +814,12 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
 
 // ---------------------------------------------------------------------------
 // Top-k for many short rows (prefill): one wave per row, four rows per block, no block
-// barriers.  Same selection as topk_radix (8 passes of 4-bit digits on lane-private LDS
-// columns, early exit), but the per-digit totals come from a 4-lane quad reduction and the
-// compaction walks the row once in index order, 64 keys per ballot, carrying the running
-// counts of selected and of equal keys (ties to the lower entry index).
+// barriers.  Same selection as topk_radix (a 4-bit digit on lane-private columns, summed by
+// 4-lane quads, then 11-, 11- and 6-bit digits on a per-wave 2048-bin histogram: lane l
+// holds 32 bins, the highest first, a wave scan finds the lane and a second one the bin;
+// early exit), and the compaction walks the row once in index order, 64 keys per ballot,
+// carrying the running counts of selected and of equal keys (ties to the lower entry
+// index).
 // Keys of lane l: indices j*64 + l; the first KPL strides stay in registers.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void lds_wave_sync() {
@@ -759,7 +845,9 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
                                                  int* __restrict__ topk_idx,
                                                  float* __restrict__ topk_score, int rows, int T,
                                                  int N_cap, int m, int k) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[4][17][64];  // row 16 unread
+  // per wave: kBins digit bins, then one spare bin per lane (keys outside the prefix); the
+  // first digit's [16][64] lane columns use the first 1024 bins
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][kBins + 64];
   __shared__ __attribute__((aligned(16))) int tots[4][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
@@ -789,25 +877,29 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
   const int n_reg = min(n_str, KPL);  // register strides in use (wave-uniform)
   const int n_inv = n_reg * 64 - min(V, n_reg * 64);
 
-  uint32_t* hc = &hist[wave][0][lane];
+  // Lane l owns the 32 bins lb .. lb + 31, lb = kBins - 32(l+1): in lane order the bins run
+  // from the highest digit down, so a wave scan of the lanes' sums counts the keys at or
+  // above each lane's bins.
+  uint32_t* hw = hist[wave];
+  const int lb = kBins - 32 * (lane + 1);
 #pragma unroll
-  for (int d = 0; d < 16; ++d) hc[d * 64] = 0;
-  // reduction role: lane = 4*d + q sums columns 16q .. 16q+15 of digit d
-  const int rd = lane >> 2, rq = lane & 3;
-  uint4* rsum = reinterpret_cast<uint4*>(&hist[wave][rd][rq * 16]);
+  for (int v = 0; v < 8; ++v) *reinterpret_cast<uint4*>(hw + lb + 4 * v) = make_uint4(0, 0, 0, 0);
 
   uint32_t prefix = 0, mask = 0;
   int remaining = kk;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 28 - 4 * pass;
+  bool done = false;
+  {  // first digit: bits 31..28 on lane-private columns hw[digit * 64 + lane]
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
-      if (j < n_reg) atomicAdd(hc + digit_row(key[j], prefix, shift) * 64, 1u);
+      if (j < n_reg) atomicAdd(hw + (key[j] >> 28) * 64 + lane, 1u);
     for (int j = KPL; j < n_str; ++j) {
       const int i = j * 64 + lane;
-      if (i < V) atomicAdd(hc + digit_row(score_key(s[i]), prefix, shift) * 64, 1u);
+      if (i < V) atomicAdd(hw + (score_key(s[i]) >> 28) * 64 + lane, 1u);
     }
     lds_wave_sync();
+    // lane 4d + q sums columns 16q .. 16q + 15 of digit d and clears them
+    const int rd = lane >> 2, rq = lane & 3;
+    uint4* rsum = reinterpret_cast<uint4*>(hw + rd * 64 + rq * 16);
     int c = 0;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -816,7 +908,7 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
       rsum[v] = make_uint4(0, 0, 0, 0);
     }
     c = quad_sum(c);
-    if (rd == 0 && prefix == 0u) c -= n_inv;  // empty register slots (key 0)
+    if (rd == 0) c -= n_inv;  // empty register slots (key 0)
     if (rq == 0) tots[wave][rd] = c;
     lds_wave_sync();
     int tv[16];
@@ -835,10 +927,53 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
       }
     }
     remaining -= above;
+    prefix = static_cast<uint32_t>(digit) << 28;
+    mask = 0xF0000000u;
+    done = in_digit == remaining;
+  }
+#pragma unroll 1
+  for (int pass = 1; pass < 4 && !done; ++pass) {
+    const int shift = radix_shift(pass), width = radix_width(pass);
+    const uint32_t spare = kBins + lane;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (j < n_reg) atomicAdd(hw + radix_bin(key[j], prefix, shift, width, spare), 1u);
+    for (int j = KPL; j < n_str; ++j) {
+      const int i = j * 64 + lane;
+      if (i < V) atomicAdd(hw + radix_bin(score_key(s[i]), prefix, shift, width, spare), 1u);
+    }
+    lds_wave_sync();
+    int lsum = 0;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const uint4 x = *reinterpret_cast<const uint4*>(hw + lb + 4 * v);
+      lsum += static_cast<int>(x.x + x.y + x.z + x.w);
+    }
+    // the n_inv empty register slots hold key 0: bin 0 while the prefix is all zeros
+    if (lb == 0 && prefix == 0u) lsum -= n_inv;
+    const int incl = wave_incl_scan(lsum);
+    const int L = __builtin_ctzll(__ballot(incl >= remaining));  // the lane holding the key
+    int above = __builtin_amdgcn_readlane(incl - lsum, L);
+    // lane L's bins from the highest down: lane i < 32 takes bin top - i
+    const int top = kBins - 32 * L - 1;
+    int c = 0;
+    if (lane < 32) {
+      c = static_cast<int>(hw[top - lane]);
+      if (top - lane == 0 && prefix == 0u) c -= n_inv;
+    }
+    const int cincl = wave_incl_scan(c);
+    const int I = __builtin_ctzll(__ballot(lane < 32 && above + cincl >= remaining));
+    const int digit = top - I;
+    const int in_digit = __builtin_amdgcn_readlane(c, I);
+    above += __builtin_amdgcn_readlane(cincl - c, I);
+    // clear the bins for the next pass (after the reads above: one wave, LDS in order)
+#pragma unroll
+    for (int v = 0; v < 8; ++v) *reinterpret_cast<uint4*>(hw + lb + 4 * v) = make_uint4(0, 0, 0, 0);
+    remaining -= above;
     prefix |= static_cast<uint32_t>(digit) << shift;
-    mask |= 15u << shift;
-    if (in_digit == remaining) break;
-    lds_wave_sync();  // tots read before the next pass rewrites them
+    mask |= ((1u << width) - 1u) << shift;
+    done = in_digit == remaining;
+    lds_wave_sync();
   }
 
   // one index-ordered walk over the row
