@@ -286,15 +286,25 @@ __device__ __forceinline__ void stream_scores(const bf16_t* __restrict__ q_idx,
     if (half == 0 && n < e1) srow[n] = part;
   };
   uint4 b0[IX_CI / 16], b1[IX_CI / 16], b2[IX_CI / 16];
+  // The Q and head-weight loads stay ahead of the key loads (the scheduler moved some after
+  // them), so that the wait below leaves only the 16 key loads in flight.  Otherwise the
+  // Q fragments and head weights count as loads still in flight inside the loop, and each
+  // use waited for every key load issued since: every sub-tile drained the queue.
+  __builtin_amdgcn_sched_barrier(0);
   load(b0, e0);
-  if (e0 + 32 < e1) load(b1, e0 + 32);
+  load(b1, e0 + 32);  // rows clamped: in bounds even past e1
+  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): Q fragments and head weights landed
+  // Every load and score of the loop is unconditional: past e1 the loads read the clamped
+  // last row (in bounds, cached) and the stores are masked.  With conditional loads the
+  // compiler's waits, merged over the paths that skip them, treated the sub-tile about to be
+  // scored as the latest load and drained the two issued after it.
   for (int n0 = e0; n0 < e1; n0 += 96) {  // wave-uniform bounds throughout
-    if (n0 + 64 < e1) load(b2, n0 + 64);
+    load(b2, n0 + 64);
     score(b0, n0);
-    if (n0 + 96 < e1) load(b0, n0 + 96);
-    if (n0 + 32 < e1) score(b1, n0 + 32);
-    if (n0 + 128 < e1) load(b1, n0 + 128);
-    if (n0 + 64 < e1) score(b2, n0 + 64);
+    load(b0, n0 + 96);
+    score(b1, n0 + 32);
+    load(b1, n0 + 128);
+    score(b2, n0 + 64);
   }
 }
 
