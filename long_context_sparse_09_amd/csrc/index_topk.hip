@@ -521,6 +521,12 @@ constexpr int kBins = 2048;
 __device__ __forceinline__ int radix_shift(int pass) { return pass == 1 ? 17 : (pass == 2 ? 6 : 0); }
 __device__ __forceinline__ int radix_width(int pass) { return pass == 3 ? 6 : 11; }
 
+// Lowest set lane of a ballot.  The digit searches always have one (the bins hold at least
+// the keys still needed); an empty ballot gives lane 63, whose bins are in range.
+__device__ __forceinline__ int first_lane(unsigned long long b) {
+  return b ? __builtin_ctzll(b) : 63;
+}
+
 // Histogram bin of a key in a radix pass: its digit at `shift` when the key carries the
 // digits chosen so far (prefix; its bits at and below the digit are 0), else `spare`, a bin
 // nobody reads.  (key ^ prefix) >> shift keeps set bits above the digit exactly for keys
@@ -717,7 +723,7 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
     }
     const int lincl = wave_incl_scan(lsum);
     const unsigned long long hit = __ballot(above + lincl >= remaining);
-    const int L = __builtin_ctzll(hit);
+    const int L = first_lane(hit);
     above += __builtin_amdgcn_readlane(lincl - lsum, L);
     int digit = 0, in_digit = 0;
     found = false;
@@ -961,7 +967,7 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
     // the n_inv empty register slots hold key 0: bin 0 while the prefix is all zeros
     if (lb == 0 && prefix == 0u) lsum -= n_inv;
     const int incl = wave_incl_scan(lsum);
-    const int L = __builtin_ctzll(__ballot(incl >= remaining));  // the lane holding the key
+    const int L = first_lane(__ballot(incl >= remaining));  // the lane holding the key
     int above = __builtin_amdgcn_readlane(incl - lsum, L);
     // lane L's bins from the highest down: lane i < 32 takes bin top - i
     const int top = kBins - 32 * L - 1;
@@ -971,7 +977,7 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
       if (top - lane == 0 && prefix == 0u) c -= n_inv;
     }
     const int cincl = wave_incl_scan(c);
-    const int I = __builtin_ctzll(__ballot(lane < 32 && above + cincl >= remaining));
+    const int I = min(first_lane(__ballot(lane < 32 && above + cincl >= remaining)), 31);
     const int digit = top - I;
     const int in_digit = __builtin_amdgcn_readlane(c, I);
     above += __builtin_amdgcn_readlane(cincl - c, I);
