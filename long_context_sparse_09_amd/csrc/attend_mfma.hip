@@ -749,27 +749,38 @@ attend_mfma_kernel(AttendArgs a) {
 // Split-mode merge: per (query, head, 4 channels), the partial outputs of the key ranges are
 // combined in the common scale of their largest running max.  Every range started from the
 // sink state (max = sink, sum = 1), so n_split - 1 copies of the sink term are removed.
+// NS ranges, a compile-time count: every range's (max, sum) pair and partial output is
+// loaded before any is used (in a loop over a run-time count each load was waited for in
+// turn).
+template <int NS>
 __global__ void __launch_bounds__(256) attend_merge_kernel(const float* __restrict__ part,
                                                            const float* __restrict__ sink,
-                                                           bf16_t* __restrict__ out, int n_q,
-                                                           int n_split) {
+                                                           bf16_t* __restrict__ out, int n_q) {
   const int gid = blockIdx.x * 256 + threadIdx.x;
   if (gid >= n_q * AH * (AD / 4)) return;
   const int q = gid / (AH * (AD / 4));
   const int h = (gid / (AD / 4)) % AH;
   const int c = (gid % (AD / 4)) * 4;
-  const float* ml = part + static_cast<size_t>(n_q) * n_split * AH * AD;
-  float mx = -INFINITY;
-  for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, ml[((q * n_split + i) * AH + h) * 2]);
+  const float* ml = part + static_cast<size_t>(n_q) * NS * AH * AD;
+  float2 mls[NS];
+  f32x4_t v[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const size_t item = static_cast<size_t>(q) * NS + i;
+    mls[i] = *reinterpret_cast<const float2*>(ml + (item * AH + h) * 2);
+    v[i] = *reinterpret_cast<const f32x4_t*>(part + (item * AH + h) * AD + c);
+  }
   const float sink2 = sink[h] * kLog2e;
-  float l = -static_cast<float>(n_split - 1) * __builtin_amdgcn_exp2f(sink2 - mx);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) mx = fmaxf(mx, mls[i].x);
+  float l = -static_cast<float>(NS - 1) * __builtin_amdgcn_exp2f(sink2 - mx);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < n_split; ++i) {
-    const size_t item = static_cast<size_t>(q) * n_split + i;
-    const float w = __builtin_amdgcn_exp2f(ml[(item * AH + h) * 2] - mx);
-    l += w * ml[(item * AH + h) * 2 + 1];
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + (item * AH + h) * AD + c);
-    acc += w * v;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const float w = __builtin_amdgcn_exp2f(mls[i].x - mx);
+    l += w * mls[i].y;
+    acc += w * v[i];
   }
   const float inv = 1.f / l;
   u32x2_t pk;
@@ -841,8 +852,15 @@ static hipError_t launch_mfma(const AttendArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int total = n_q * AH * (AD / 4);
-    hipLaunchKernelGGL(attend_merge_kernel, dim3((total + 255) / 256), dim3(256), 0, st, a.part,
-                       a.sink, static_cast<bf16_t*>(a.out), n_q, a.n_split);
+    const dim3 grid((total + 255) / 256);
+    bf16_t* out = static_cast<bf16_t*>(a.out);
+    switch (a.n_split) {
+#define MERGE(ns) \
+  case ns: hipLaunchKernelGGL(attend_merge_kernel<ns>, grid, dim3(256), 0, st, a.part, a.sink, out, n_q); break;
+      MERGE(2) MERGE(3) MERGE(4) MERGE(5) MERGE(6) MERGE(7) MERGE(8)
+#undef MERGE
+      default: return hipErrorInvalidValue;  // attend_split_count gives 1 .. kMaxSplit
+    }
   }
   return hipGetLastError();
 }
