@@ -370,6 +370,20 @@ def test_split_attend_csa_two_queries_per_sequence():
                  k=128, seed=30, split=True, shuffle_invalid=True)
 
 
+@pytest.mark.parametrize("ns", [2, 3, 5, 6, 7])
+def test_split_attend_every_range_count(ns):
+    # the merge is compiled once per range count (2 .. 8), and the count is the device's
+    # compute units over the queries: these query counts give each remaining count once (8 and
+    # 4 come from the tests above and the 64-sequence decode)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B = cus // ns
+    if B < 1 or min(8, cus // B) != ns:
+        pytest.skip(f"{cus} compute units give no query count with {ns} ranges")
+    L_b = [300 + 37 * b for b in range(B)]
+    _attend_case("bf16", True, B, 1, 64, 512, 64, 128, 128, [x - 128 for x in L_b],
+                 [x - 1 for x in L_b], 200, k=64, seed=40 + ns, split=True)
+
+
 @pytest.mark.parametrize("k", [510, 6, 509])
 @pytest.mark.parametrize("split", [False, True])
 def test_csa_attend_list_length_not_multiple_of_4(k, split):
