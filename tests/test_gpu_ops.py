@@ -263,6 +263,15 @@ def test_index_topk_small_T_stream_path():
     _topk_case("bf16", 2, 3, 64, 128, 3000, 300, 4, [7001, 4096], [1800, 3000], 12)
 
 
+def test_index_topk_many_rows_past_registers():
+    # 2048 rows of ~5000-5500 entries on a 9000-entry pool: the one-wave-per-row selection,
+    # whose key strides past the 64 it holds in registers are re-read from the score row on
+    # every pass (the fp32 generic scorer keeps the oracle cheap); then the same rows with only
+    # 6 distinct scores, so that the k-th slot lies inside thousands of exact ties
+    _topk_case("fp32", 1, 2048, 4, 32, 9000, 64, 4, [20000], [9000], 17)
+    _topk_case("fp32", 1, 2048, 4, 32, 9000, 64, 4, [20000], [9000], 18, few_rows=(0,))
+
+
 def test_index_topk_exact_ties():
     _topk_case("bf16", 1, 40, 64, 128, 60, 16, 4, [300], [60], 9, ties=True)
     _topk_case("fp32", 1, 40, 4, 32, 60, 16, 4, [300], [60], 10, ties=True)
