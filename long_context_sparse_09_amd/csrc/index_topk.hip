@@ -501,7 +501,9 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
 // the other is read; two barriers per pass.
 //
 // Output: index-ordered compaction through LDS bitmaps, segment by segment (32768 indices):
-// one bit per key above the threshold and one per key equal to it (both from wave ballots),
+// one bit per key above the threshold and one per key equal to it (both from wave ballots;
+// a wave collects the two words of its register stride j in lanes 2j, 2j + 1 and writes
+// them with one LDS store per lane),
 // a block scan of the equal-key popcounts keeps the lowest-index equal keys that are needed
 // (ties to the lower entry index), and a block scan of the selected popcounts gives every
 // word its output offset.
@@ -575,6 +577,10 @@ __device__ __forceinline__ int block_scan_excl(int v, int* total, int* wsum) {
   return before + incl - v;
 }
 
+// v_writelane: lane `lane` of `old` replaced by the wave-uniform `src` (the LLVM intrinsic,
+// declared by name; the compiler inserts the wait states its SGPR operands need)
+extern "C" __device__ int lane_write(int src, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
 constexpr int kSegIdx = 32768;          // indices per compaction segment
 constexpr int kSegWords = kSegIdx / 32;  // bitmap words per segment
 
@@ -588,6 +594,7 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
   constexpr int NW = NT / 64;
   static_assert(kSegIdx % NT == 0 && NT % 64 == 0, "segment = whole block strides");
   static_assert(KPT * NT <= kSegIdx, "register keys must fit the first segment");
+  static_assert(2 * KPT <= 64, "a wave's bitmap words of the register strides: one per lane");
   // two histograms used in alternate passes: kBins digit bins, then one spare bin per lane
   __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins + 64];
   __shared__ uint32_t gtbits[kSegWords], eqbits[kSegWords];
@@ -746,17 +753,22 @@ __global__ void __launch_bounds__(NT) topk_radix(const float* __restrict__ score
     const int seg_end = min(V, seg0 + kSegIdx);
     const int j0 = seg0 / NT, j1 = (seg_end + NT - 1) / NT;
     if (seg0 == 0) {  // register keys all lie in the first segment (KPT * NT <= kSegIdx)
+      int gw = 0, ew = 0;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const bool ok = key[j] != 0u;
         const uint32_t km = key[j] & mask;
         const unsigned long long g = __ballot(ok && km > prefix);
         const unsigned long long e = __ballot(ok && km == prefix);
-        if (lane < 2) {
-          const int w = j * (NT / 32) + wave * 2 + lane;
-          gtbits[w] = static_cast<uint32_t>(lane ? g >> 32 : g);
-          eqbits[w] = static_cast<uint32_t>(lane ? e >> 32 : e);
-        }
+        gw = lane_write(static_cast<int>(g), 2 * j, gw);
+        gw = lane_write(static_cast<int>(g >> 32), 2 * j + 1, gw);
+        ew = lane_write(static_cast<int>(e), 2 * j, ew);
+        ew = lane_write(static_cast<int>(e >> 32), 2 * j + 1, ew);
+      }
+      if (lane < 2 * KPT) {
+        const int w = (lane >> 1) * (NT / 32) + wave * 2 + (lane & 1);
+        gtbits[w] = static_cast<uint32_t>(gw);
+        eqbits[w] = static_cast<uint32_t>(ew);
       }
     }
     for (int j = max(j0, KPT); j < j1; ++j) {
@@ -1009,14 +1021,30 @@ __global__ void __launch_bounds__(256) topk_wave(const float* __restrict__ score
     }
     out_pos += __popcll(sb);
   };
+  // the search ended on a whole bucket: every key at or above the prefix is kept (a key
+  // compares with the prefix as its masked value does, the prefix being zero below the mask)
+  auto emit_ge = [&](int i, bool ok, uint32_t kj) {
+    const bool sel = ok && kj >= prefix;
+    const unsigned long long sb = __ballot(sel);
+    const int pos = out_pos + __popcll(sb & below);
+    if (sel && pos < k) {
+      out_i[pos] = i;
+      if (out_s) out_s[pos] = key_score(kj);
+    }
+    out_pos += __popcll(sb);
+  };
+  auto walk = [&](auto&& f) {
 #pragma unroll
-  for (int j = 0; j < KPL; ++j)
-    if (j < n_str) emit(j * 64 + lane, key[j] != 0u, key[j]);
-  for (int j = KPL; j < n_str; ++j) {
-    const int i = j * 64 + lane;
-    const bool ok = i < V;
-    emit(i, ok, ok ? score_key(s[i]) : 0u);
-  }
+    for (int j = 0; j < KPL; ++j)
+      if (j < n_str) f(j * 64 + lane, key[j] != 0u, key[j]);
+    for (int j = KPL; j < n_str; ++j) {
+      const int i = j * 64 + lane;
+      const bool ok = i < V;
+      f(i, ok, ok ? score_key(s[i]) : 0u);
+    }
+  };
+  if (done) walk(emit_ge);
+  else walk(emit);
   for (int p = kk + lane; p < k; p += 64) {
     out_i[p] = -1;
     if (out_s) out_s[p] = 0.f;
