@@ -270,17 +270,19 @@ __global__ void __launch_bounds__(64) compress_window_kernel(
 // ---------------------------------------------------------------------------
 // compress, disjoint windows at a large rate (HCA, m = NG * GS slots, bf16, C = 512): one
 // workgroup per entry, NG wavefronts; wavefront p pools slots [p GS, (p + 1) GS) for all 512
-// channels (lane l owns channels 8l .. 8l + 7), in groups of 8 tokens whose loads (values,
-// gates, slot biases) are all issued before the group's arithmetic.  A group is pooled in two
-// passes (maximum, then exponentials) and merged into the wavefront's running state; the NG
-// states of a channel are merged through LDS by wavefront 0, which also applies RoPE.
+// channels (lane l owns channels 8l .. 8l + 7), in groups of 4 tokens.  The loads of group
+// g + 1 (values, gates, slot biases) are issued before group g's arithmetic, so a wavefront
+// always has a group in flight; HB (slot biases given) is a template parameter, so no load is
+// conditional and the waits cover exactly the group about to be pooled.  A group is pooled in
+// two passes (maximum, then exponentials) and merged into the wavefront's running state; the
+// NG states of a channel are merged through LDS by wavefront 0, which also applies RoPE.
 // ---------------------------------------------------------------------------
-template <int NG, int GS>
+template <int NG, int GS, bool HB>
 __global__ void __launch_bounds__(NG * 64) compress_disjoint_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ gate, const float* __restrict__ bias,
     bf16_t* __restrict__ pool, int S, int e0, int N_cap, int r, const RopeFreq rf, long long pos_off) {
-  constexpr int C = 512, VEC = 8, M = NG * GS, U = 8;
-  static_assert(GS % U == 0, "slot groups of 8");
+  constexpr int C = 512, VEC = 8, M = NG * GS, U = 4;
+  static_assert(GS % U == 0, "slot groups of 4");
   __shared__ float red[NG][3][VEC][64];  // per wavefront: max, sum, acc of each lane's channels
   __shared__ double inv_freq[kMaxRope / 2];
   for (int i = threadIdx.x; i < r / 2; i += NG * 64) inv_freq[i] = rf.inv[i];
@@ -300,16 +302,25 @@ __global__ void __launch_bounds__(NG * 64) compress_disjoint_kernel(
       v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
     }
   };
-#pragma unroll 1
-  for (int s0 = p * GS; s0 < (p + 1) * GS; s0 += U) {
-    uint4 xr[U], gr[U];
-    float bv[U][VEC];
+  uint4 xq[2][U], gq[2][U];
+  float bq[2][U][VEC];
+  auto load_group = [&](int s0, int k) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      xr[u] = *reinterpret_cast<const uint4*>(xb + static_cast<size_t>(s0 + u) * C);
-      gr[u] = *reinterpret_cast<const uint4*>(gb + static_cast<size_t>(s0 + u) * C);
-      if (bias != nullptr) Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s0 + u) * C + c0, bv[u]);
+      xq[k][u] = *reinterpret_cast<const uint4*>(xb + static_cast<size_t>(s0 + u) * C);
+      gq[k][u] = *reinterpret_cast<const uint4*>(gb + static_cast<size_t>(s0 + u) * C);
+      if constexpr (HB) Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s0 + u) * C + c0, bq[k][u]);
     }
+  };
+  load_group(p * GS, 0);
+#pragma unroll
+  for (int kg = 0; kg < GS / U; ++kg) {
+    const int s0 = p * GS + kg * U;
+    if (kg + 1 < GS / U) load_group(s0 + U, (kg + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);  // the next group's loads stay ahead of this fold
+    const uint4 (&xr)[U] = xq[kg & 1];
+    const uint4 (&gr)[U] = gq[kg & 1];
+    const float (&bv)[U][VEC] = bq[kg & 1];
     float a[U][VEC], gm[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) gm[i] = -INFINITY;
@@ -319,7 +330,7 @@ __global__ void __launch_bounds__(NG * 64) compress_disjoint_kernel(
       unpack(gr[u], gv);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
-        a[u][i] = (bias != nullptr ? gv[i] + bv[u][i] : gv[i]) * kLog2e;
+        a[u][i] = (HB ? gv[i] + bv[u][i] : gv[i]) * kLog2e;
         gm[i] = fmaxf(gm[i], a[u][i]);
       }
     }
@@ -392,9 +403,14 @@ hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, 
     return hipGetLastError();
   }
   if (dtype == 1 && !overlap && m == 128 && C == 512 && e1 > e0) {
-    hipLaunchKernelGGL((compress_disjoint_kernel<8, 16>), dim3(e1 - e0, B), dim3(512), 0, st,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gate), bias,
-                       static_cast<bf16_t*>(pool), S, e0, N_cap, r, make_rope_freq(r, theta), off);
+    if (bias != nullptr)
+      hipLaunchKernelGGL((compress_disjoint_kernel<8, 16, true>), dim3(e1 - e0, B), dim3(512), 0, st,
+                         static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gate), bias,
+                         static_cast<bf16_t*>(pool), S, e0, N_cap, r, make_rope_freq(r, theta), off);
+    else
+      hipLaunchKernelGGL((compress_disjoint_kernel<8, 16, false>), dim3(e1 - e0, B), dim3(512), 0, st,
+                         static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gate), bias,
+                         static_cast<bf16_t*>(pool), S, e0, N_cap, r, make_rope_freq(r, theta), off);
     return hipGetLastError();
   }
   if (dtype == 1) {
