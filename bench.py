@@ -247,7 +247,7 @@ def run_csa_prefill(torch, clock, steps, warmup):
 
 def run_hca_prefill(torch, clock, steps, warmup):
     import workloads as W
-    from long_context_sparse_09_amd import csa_compress, hca_attend, layers, swa_concat
+    from long_context_sparse_09_amd import csa_compress, hca_attend, hca_attend_pairs, layers, swa_concat
 
     w = W.workload(3)
     S = w.S
@@ -279,6 +279,10 @@ def run_hca_prefill(torch, clock, steps, warmup):
     b_cmp = compress_bytes(S, w.D, w.m_hca, False, N)
     b_swa = 2 * S * w.D * 2
     st = time_ops(clock, ops, {"hca_compress": b_cmp, "swa_concat": b_swa, "hca_attend": b_att})
+    # the query-pair kernel on the same inputs, for comparison (not part of the step)
+    pairs = {"hca_attend_pairs": lambda: hca_attend_pairs(inp["q"], buf.kv_win, z, buf.pool_h, buf.n_pool_h,
+                                                          w.m_hca, inp["sink"], z, buf.out, w.W, w.r, w.base)}
+    st.update(time_ops(clock, pairs, {"hca_attend_pairs": b_att}))
     del inp, buf
     return {
         "workload": w.name, "query_tokens_per_s": S / wall, "ms_per_step": wall * 1e3,
@@ -288,6 +292,8 @@ def run_hca_prefill(torch, clock, steps, warmup):
             # AI = 380 flop/B, near the ridge (315): both fractions are reported
             "hca_attend": kernel_entry(st["hca_attend"], "mfma", alg_flops=fl, alg_bytes=b_att,
                                        keys_per_query=float(keys.mean())),
+            "hca_attend_pairs (comparison, not in the step)": kernel_entry(
+                st["hca_attend_pairs"], "mfma", alg_flops=fl, alg_bytes=b_att),
         },
     }
 

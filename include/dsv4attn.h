@@ -255,6 +255,21 @@ int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
                size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * hca_attend_pairs - hca_attend (same keys, same result up to fp32 rounding order) computed
+ * by the query-pair kernel: two consecutive queries of a sequence share every 32-key tile,
+ * which is read from LDS by 2 x 64 query-head rows ("Attention mask layout", HCA paragraph:
+ * neighbouring queries see the same entries and all but one window row each).  Covers bf16,
+ * H = 64, D = 512, rope_dim 0 or 64 (DSV4_ERR_UNSUPPORTED otherwise); no workspace.  On
+ * gfx950 at these shapes hca_attend is faster: each of the pair kernel's four waves must issue
+ * its share of the key-row copies itself, and a wave stalls ~200 cycles per 1 KB copy it issues.
+ */
+int hca_attend_pairs(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
+                     int N_cap, const int* n_pool, int m_hca, const float* sink, const int* q_pos0,
+                     void* out, int B, int T, int H, int D, int window, int rope_dim,
+                     double rope_theta, long long rope_pos_offset, float scale, int dtype,
+                     void* stream);
+
+/*
  * grouped_out_proj - grouped low-rank output projection ("Hybrid attention (§2.3)", grouped
  * output projection item; "DeepseekV4Config": o_groups, o_lora_rank, hidden_size).  Reading:
  * head group g is the run of H/groups consecutive heads; its concatenated outputs

@@ -13,7 +13,7 @@ from typing import Optional
 from . import _lib
 
 __all__ = ["csa_compress", "compressor_cache_update", "csa_index_topk",
-           "csa_index_topk_workspace_size", "csa_index_topk_noalloc", "NOALLOC_SCRATCH_BYTES", "swa_concat", "csa_attend", "hca_attend",
+           "csa_index_topk_workspace_size", "csa_index_topk_noalloc", "NOALLOC_SCRATCH_BYTES", "swa_concat", "csa_attend", "hca_attend", "hca_attend_pairs",
            "attend_workspace_size", "grouped_out_proj", "linear_bt", "linear_bt_multi", "input_projections", "attention_mask_dump",
            "abi_version", "DSV4Error", "lib"]
 
@@ -200,6 +200,18 @@ def hca_attend(q, kv_win, kv_pos0, pool, n_pool, m_hca: int, sink, q_pos0, out, 
         m_hca, _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D, window, rope_dim,
         float(rope_theta), int(rope_pos_offset), float(scale), wp, wb, _dtype(q),
         _stream(stream)))
+
+
+def hca_attend_pairs(q, kv_win, kv_pos0, pool, n_pool, m_hca: int, sink, q_pos0, out, window: int,
+                     rope_dim: int, rope_theta: float, rope_pos_offset: int = 0, scale: float = 0.0,
+                     stream=None) -> None:
+    """hca_attend computed by the query-pair kernel (bf16, 64 heads x 512 only)."""
+    B, T, H, D = q.shape
+    N_cap = 0 if pool is None else pool.shape[1]
+    _check("hca_attend_pairs", lib().hca_attend_pairs(
+        _ptr(q), _ptr(kv_win), _ptr(kv_pos0), kv_win.shape[1], _ptr(pool), N_cap, _ptr(n_pool),
+        m_hca, _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D, window, rope_dim,
+        float(rope_theta), int(rope_pos_offset), float(scale), _dtype(q), _stream(stream)))
 
 
 def grouped_out_proj(attn, w_a, w_b, mid, out, stream=None) -> None:

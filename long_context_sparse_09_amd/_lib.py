@@ -55,6 +55,9 @@ SIGNATURES = {
     "hca_attend": ([c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_int,
                     c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
                     c_double, c_ll, c_float, c_void_p, c_size_t, c_int, c_void_p], c_int),
+    "hca_attend_pairs": ([c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_int,
+                          c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
+                          c_double, c_ll, c_float, c_int, c_void_p], c_int),
 }
 
 _lib = None

@@ -408,4 +408,19 @@ int hca_attend(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, 
   return attend_common(a, workspace, workspace_bytes, stream, "hca_attend");
 }
 
+int hca_attend_pairs(const void* q, const void* kv_win, const int* kv_pos0, int S_kv, const void* pool,
+                     int N_cap, const int* n_pool, int m_hca, const float* sink, const int* q_pos0,
+                     void* out, int B, int T, int H, int D, int window, int rope_dim,
+                     double rope_theta, long long rope_pos_offset, float scale, int dtype,
+                     void* stream) {
+  REQUIRE(m_hca >= 1, "m_hca must be >= 1");
+  dsv4::AttendArgs a{q, kv_win, kv_pos0, S_kv, pool, N_cap, nullptr, 0, n_pool, m_hca, sink, q_pos0,
+                     out, B, T, H, D, window, rope_dim, rope_theta, rope_pos_offset, scale, dtype, false,
+                     {}};
+  if (!dsv4::attend_dense_fits(a))
+    return fail(DSV4_ERR_UNSUPPORTED, "hca_attend_pairs covers bf16, H = 64, D = 512, rope_dim 0 or 64 only");
+  a.pairs = true;
+  return attend_common(a, nullptr, 0, stream, "hca_attend_pairs");
+}
+
 }  // extern "C"

@@ -867,6 +867,7 @@ static hipError_t launch_mfma(const AttendArgs& a, hipStream_t st) {
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (a.B == 0 || a.T == 0) return hipSuccess;
+  if (a.pairs) return launch_attend_dense(a, st);  // shape checked by the caller
   if (attend_uses_fast(a)) {
     if (a.r == 64) return a.csa ? launch_mfma<true, 64>(a, st) : launch_mfma<false, 64>(a, st);
     return a.csa ? launch_mfma<true, 0>(a, st) : launch_mfma<false, 0>(a, st);

@@ -74,6 +74,8 @@ struct AttendArgs {
   // [items][H][2], merged by a second kernel.  n_split = 1: part unused.
   int n_split;
   float* part;
+  // hca_attend_pairs: the query-pair kernel (two consecutive queries share each key tile)
+  bool pairs;
 };
 
 // Key ranges per query the split mode uses for n_q queries on this device (1: no split), and
@@ -82,6 +84,11 @@ int attend_split_count(int n_q);
 size_t attend_split_bytes(int n_q);
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+// Dense-range attention over query pairs (HCA and sliding layers): whether the kernel covers a
+// shape, and the launch.
+bool attend_dense_fits(const AttendArgs& a);
+hipError_t launch_attend_dense(const AttendArgs& a, hipStream_t st);
 
 // Whether the MFMA fast paths cover a shape (otherwise the generic kernels run).
 bool index_scores_fast(int nI, int cI, int dtype);

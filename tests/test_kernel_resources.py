@@ -18,6 +18,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 KERNELS = {  # source file -> mangled-name fragments of kernels that must not use scratch
     "attend_mfma.hip": ["attend_mfma_kernel"],
+    "attend_dense.hip": ["attend_dense_kernel"],
     "index_topk.hip": ["index_score_mfma", "index_score_stream", "topk_wave", "topk_radix"],
 }
 
