@@ -268,6 +268,124 @@ __global__ void __launch_bounds__(64) compress_window_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// compress, overlapping windows (CSA, m = M, bf16, C a multiple of 128): LDS-staged.  A
+// workgroup of WPB wavefronts pools NE = WPB * (64 / G) consecutive entries w0 .. w0 + NE - 1
+// (G = C/8 lanes per entry, 8 channels a lane).  Their windows cover the contiguous token rows
+// [(w0 - 1) M, (w0 + NE) M), one contiguous span of each input, which the workgroup first
+// copies into LDS with straight 1 KB buffer loads (buffer_load ... lds): every token is read
+// from memory once per workgroup (plus an M-row halo) instead of once per window that holds
+// it, in fully coalesced 1 KB pieces.  Rows outside the sequence read as zeros; only absent
+// slots (before token 0) or entries past e1 (not stored) touch them.  Each entry is then
+// pooled from LDS as the register-window kernel pools it: two-pass softmax over the 2M slots
+// with the slot biases in the log2 domain, RoPE epilogue.
+// ---------------------------------------------------------------------------
+template <int M, int WPB>
+__global__ void __launch_bounds__(64 * WPB) compress_staged_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ gate, const float* __restrict__ bias,
+    bf16_t* __restrict__ pool, int S, int C, int e0, int e1, int N_cap, int r, const RopeFreq rf,
+    long long pos_off, int G, int n_blocks, int blocks_per_xcd) {
+  constexpr int VEC = 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char stg[];  // [x | gate][rows][C] bf16
+  __shared__ double inv_freq[kMaxRope / 2];
+  for (int i = threadIdx.x; i < r / 2; i += 64 * WPB) inv_freq[i] = rf.inv[i];
+  const int lb = (blockIdx.x % 8) * blocks_per_xcd + blockIdx.x / 8;  // consecutive blocks on one XCD
+  if (lb >= n_blocks) return;  // block-uniform, before any barrier
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int NE = WPB * (64 / G);
+  const int w0 = e0 + lb * NE;
+  const int row_bytes = C * 2;
+  const int span = (NE + 1) * M * row_bytes;  // bytes of one input's token span (a multiple of 1 KB)
+  // the span starts at token (w0 - 1) M; offsets are taken from the sequence's first row, so
+  // the rows before it (w0 = 0) have negative offsets, which wrap past the descriptor's end
+  const int start = (w0 - 1) * M * row_bytes;
+  const unsigned seq_bytes = static_cast<unsigned>(S) * static_cast<unsigned>(row_bytes);
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(x + static_cast<size_t>(b) * S * C), static_cast<short>(0), static_cast<int>(seq_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t g_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(gate + static_cast<size_t>(b) * S * C), static_cast<short>(0), static_cast<int>(seq_bytes), 0x00020000);
+  const int n_kb = span / 1024;
+  for (int k = wave; k < n_kb; k += WPB) {
+    const unsigned off = static_cast<unsigned>(start + k * 1024 + lane * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void_t*)(stg + k * 1024), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rs, (lds_void_t*)(stg + span + k * 1024), 16, off, 0, 0, 0);
+  }
+  // slot biases (log2 domain) while the span lands
+  const int g = lane % G;
+  const int c0 = g * VEC;
+  float bz[2 * M][VEC];
+  if (bias != nullptr) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2 * M; ++s2)
+      Chunk<float>::template load<VEC>(bias + static_cast<size_t>(s2) * C + c0, bz[s2]);
+#pragma unroll
+    for (int s2 = 0; s2 < 2 * M; ++s2)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) bz[s2][i] *= kLog2e;
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < 2 * M; ++s2)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) bz[s2][i] = 0.f;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  __syncthreads();                     // and every wave's
+  const int e = wave * (64 / G) + lane / G;  // this stream's entry within the block
+  const int w = w0 + e;
+  if (w >= e1) return;  // no barrier follows
+  auto unpack = [](const uint4& u, float (&v)[VEC]) {
+    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(wd[i] << 16);
+      v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+    }
+  };
+  // slot s2 of entry e is span row e M + s2
+  const unsigned char* xs = stg + (e * M) * row_bytes + c0 * 2;
+  const unsigned char* gs = xs + span;
+  float a[2 * M][VEC];
+  float mx[VEC];
+#pragma unroll
+  for (int ch = 0; ch < VEC; ++ch) mx[ch] = -INFINITY;
+#pragma unroll
+  for (int s2 = 0; s2 < 2 * M; ++s2) {
+    float gv[VEC];
+    unpack(*reinterpret_cast<const uint4*>(gs + s2 * row_bytes), gv);
+    const bool present = (w - 1) * M + s2 >= 0;
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch) {
+      a[s2][ch] = present ? fmaf(gv[ch], kLog2e, bz[s2][ch]) : -INFINITY;
+      mx[ch] = fmaxf(mx[ch], a[s2][ch]);
+    }
+  }
+  float sum[VEC], acc[VEC];
+#pragma unroll
+  for (int ch = 0; ch < VEC; ++ch) {
+    sum[ch] = 0.f;
+    acc[ch] = 0.f;
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < 2 * M; ++s2) {
+    float xv[VEC];
+    unpack(*reinterpret_cast<const uint4*>(xs + s2 * row_bytes), xv);
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch) {
+      const float p = __builtin_amdgcn_exp2f(a[s2][ch] - mx[ch]);  // 0 for absent slots
+      sum[ch] += p;
+      acc[ch] = fmaf(p, xv[ch], acc[ch]);
+    }
+  }
+  float out[VEC];
+#pragma unroll
+  for (int ch = 0; ch < VEC; ++ch) out[ch] = acc[ch] * __builtin_amdgcn_rcpf(sum[ch]);
+  const double pos = static_cast<double>((static_cast<long long>(w) + 1) * M - 1 + pos_off);
+  rope_chunk<VEC, true>(out, c0, C, r, pos, inv_freq);
+  Chunk<bf16_t>::template store<VEC>(pool + (static_cast<size_t>(b) * N_cap + w) * C + c0, out);
+}
+
+// ---------------------------------------------------------------------------
 // compress, disjoint windows at a large rate (HCA, m = NG * GS slots, bf16, C = 512): one
 // workgroup per entry, NG wavefronts; wavefront p pools slots [p GS, (p + 1) GS) for all 512
 // channels (lane l owns channels 8l .. 8l + 7), in groups of 4 tokens.  The loads of group
@@ -389,6 +507,31 @@ hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, 
                            int e1, int N_cap, int r, double theta, long long off, int dtype, hipStream_t st) {
   const bool v8 = (C % 8 == 0) && (C / 8 <= 256);
   if (!overlap) x_prev = gate_prev = nullptr;  // no earlier half
+  if (dtype == 1 && overlap && m == 4 && x_prev == nullptr && C % 128 == 0 && C <= 512 && e1 > e0 &&
+      static_cast<long long>(S) * C * 2 < (1LL << 31)) {
+    // four entries per workgroup: one wavefront at C = 128 (four entries a wavefront), four
+    // at C = 512, so that 2048 entries make 512 workgroups either way
+    const int G = C / 8;
+    const int wpb = C >= 512 ? 4 : (C >= 256 ? 2 : 1);
+    const int NE = wpb * (64 / G);
+    const int nb = static_cast<int>(div_up(static_cast<uint32_t>(e1 - e0), NE));
+    const int per = static_cast<int>(div_up(static_cast<uint32_t>(nb), 8));
+    const size_t lds = 2 * static_cast<size_t>(NE + 1) * 4 * C * 2;
+    const RopeFreq rfq = make_rope_freq(r, theta);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* gb = static_cast<const bf16_t*>(gate);
+    bf16_t* pb = static_cast<bf16_t*>(pool);
+    if (wpb == 4)
+      hipLaunchKernelGGL((compress_staged_kernel<4, 4>), dim3(8 * per, B), dim3(256), lds, st, xb, gb, bias, pb, S,
+                         C, e0, e1, N_cap, r, rfq, off, G, nb, per);
+    else if (wpb == 2)
+      hipLaunchKernelGGL((compress_staged_kernel<4, 2>), dim3(8 * per, B), dim3(128), lds, st, xb, gb, bias, pb, S,
+                         C, e0, e1, N_cap, r, rfq, off, G, nb, per);
+    else
+      hipLaunchKernelGGL((compress_staged_kernel<4, 1>), dim3(8 * per, B), dim3(64), lds, st, xb, gb, bias, pb, S,
+                         C, e0, e1, N_cap, r, rfq, off, G, nb, per);
+    return hipGetLastError();
+  }
   if (dtype == 1 && overlap && m == 4 && x_prev == nullptr && C % 8 == 0 && C / 8 <= 64 &&
       64 % (C / 8) == 0 && e1 > e0) {
     constexpr int E = 1;  // entries per stream (1: twice the wavefronts of 2, measured faster)
