@@ -147,7 +147,8 @@ __device__ __forceinline__ void qk_mfma(df32x16_t& s, const dbf16x8_t& a, const 
 // operation before the next LDS reads (it cannot tell that the copy does not touch what they
 // read), which drained the tiles in flight every step.  Every consumer of the tiles waits for
 // them explicitly (vmcnt + workgroup barrier).  The descriptor and M0 are written by scalar
-// code; five wait states precede the load.
+// code (M0 set by the compiler from the asm's input operand); five wait states precede the
+// load.
 typedef __attribute__((ext_vector_type(4))) unsigned dsu32x4_t;
 __device__ __forceinline__ void dma_row(const void* src, unsigned char* dst, unsigned voff) {
   const unsigned long long p = reinterpret_cast<unsigned long long>(src);
@@ -158,10 +159,10 @@ __device__ __forceinline__ void dma_row(const void* src, unsigned char* dst, uns
   rs[3] = kWord3;
   const unsigned m0 = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned>(reinterpret_cast<uintptr_t>((dlds_void*)dst)));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(m0), "v"(voff), "s"(rs)
-               : "memory", "m0");
+               : "v"(voff), "s"(rs), "{m0}"(m0)
+               : "memory");
 }
 
 // One work item: a pair of consecutive queries t0, t0 + 1 of sequence b (or t0 alone at the
