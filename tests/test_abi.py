@@ -123,6 +123,18 @@ def test_attend_argument_errors(lib):
     assert hca(T=0) == OK
     assert hca() == INVALID
 
+    def pairs(**kw):  # the query-pair variant: bf16 64 x 512 (rope 0 or 64) only
+        a = dict(m=128, B=1, T=4, H=64, D=512, r=64, dt=BF16)
+        a.update(kw)
+        return lib.hca_attend_pairs(None, None, None, 128, None, 512, None, a["m"], None, None, None,
+                                    a["B"], a["T"], a["H"], a["D"], 128, a["r"], 1e4, 0, 0.0, a["dt"], None)
+    assert pairs(m=0) == INVALID
+    assert pairs(H=8) == UNSUPPORTED
+    assert pairs(r=32) == UNSUPPORTED
+    assert pairs(dt=FP32) == UNSUPPORTED
+    assert pairs(T=0) == OK
+    assert pairs() == INVALID  # null pointers
+
 
 def test_swa_argument_errors(lib):
     def call(**kw):
