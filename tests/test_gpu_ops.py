@@ -43,6 +43,7 @@ COMPRESS_CASES = [
     ("bf16", 1, 700, 512, 128, False, 64, False, None),  # HCA, no bias
     ("bf16", 1, 300, 512, 4, True, 64, True, (20, 41)),  # entry sub-range (chunked prefill)
     ("bf16", 1, 90, 96, 3, True, 8, False, None),      # odd rate
+    ("bf16", 2, 515, 64, 4, True, 16, True, None),     # m=4 at C=64: the register-window kernel
 ]
 
 
