@@ -36,6 +36,12 @@
 //     queries, the ragged last tile) are masked per key on the tiles that hold them.
 //   * Persistent workgroups, pairs heaviest first, consecutive pairs on one XCD (they share
 //     window rows in its L2).
+//
+// This kernel serves hca_attend_pairs.  hca_attend keeps the per-query kernel: with one wave
+// per SIMD every wave issues its share of the key-row copies, a wave stalls ~200 cycles per
+// 1 KB copy it issues, and nothing else keeps its SIMD's matrix core busy meanwhile, while the
+// per-query kernel gives the copies to waves of their own (HCA S=65536: 5.7 ms here, 4.6 ms
+// per query).
 #include "common.h"
 #include "launch.h"
 
