@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(64 * WPB) compress_staged_kernel(
   __syncthreads();                     // and every wave's
   const int e = wave * (64 / G) + lane / G;  // this stream's entry within the block
   const int w = w0 + e;
-  if (w >= e1) return;  // no barrier follows
+  if (w >= e1 || lane >= (64 / G) * G) return;  // no barrier follows
   auto unpack = [](const uint4& u, float (&v)[VEC]) {
     const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -507,8 +507,8 @@ hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, 
                            int e1, int N_cap, int r, double theta, long long off, int dtype, hipStream_t st) {
   const bool v8 = (C % 8 == 0) && (C / 8 <= 256);
   if (!overlap) x_prev = gate_prev = nullptr;  // no earlier half
-  if (dtype == 1 && overlap && m == 4 && x_prev == nullptr && C % 128 == 0 && C <= 512 && e1 > e0 &&
-      static_cast<long long>(S) * C * 2 < (1LL << 31)) {
+  if (dtype == 1 && overlap && m == 4 && x_prev == nullptr && C % 128 == 0 && C <= 512 && 64 % (C / 8) == 0 &&
+      e1 > e0 && static_cast<long long>(S) * C * 2 < (1LL << 31)) {
     // four entries per workgroup: one wavefront at C = 128 (four entries a wavefront), four
     // at C = 512, so that 2048 entries make 512 workgroups either way
     const int G = C / 8;
