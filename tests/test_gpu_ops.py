@@ -44,6 +44,8 @@ COMPRESS_CASES = [
     ("bf16", 1, 300, 512, 4, True, 64, True, (20, 41)),  # entry sub-range (chunked prefill)
     ("bf16", 1, 90, 96, 3, True, 8, False, None),      # odd rate
     ("bf16", 2, 515, 64, 4, True, 16, True, None),     # m=4 at C=64: the register-window kernel
+    ("bf16", 1, 301, 256, 4, True, 32, True, None),    # staged, two wavefronts per workgroup
+    ("bf16", 1, 203, 384, 4, True, 64, True, None),    # 48-lane chunks: the generic kernel
 ]
 
 
