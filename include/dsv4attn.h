@@ -113,6 +113,21 @@ int compressor_cache_update(const void* x_new, const void* gate_new, void* x_rin
                             void* stream);
 
 /*
+ * compressor_cache_update_pair - two compressor_cache_update calls in one launch, for the two
+ * compressors of one layer that share lengths, m, overlap and N_cap ("Cache layers": the CSA
+ * cache's compressor and the parallel indexer's).  Compressor 1 is (x_new, gate_new, x_ring,
+ * gate_ring, bias, pool, C, rope_dim), compressor 2 the same with suffix 2; each exactly as
+ * compressor_cache_update defines it, with the same argument rules (both must pass them,
+ * else nothing is launched).  The two compressors' buffers must not overlap.
+ */
+int compressor_cache_update_pair(const void* x_new, const void* gate_new, void* x_ring, void* gate_ring,
+                                 const float* bias, void* pool, int C, int rope_dim, const void* x2_new,
+                                 const void* gate2_new, void* x2_ring, void* gate2_ring, const float* bias2,
+                                 void* pool2, int C2, int rope_dim2, const int* lengths, int B, int m, int overlap,
+                                 int N_cap, double rope_theta, long long rope_pos_offset, int emit, int dtype,
+                                 void* stream);
+
+/*
  * csa_compress_split - csa_compress with separate projections for the two halves of each
  * overlapping window (reading R4b of the CSA compressor: the earlier half of entry w's window,
  * tokens (w-1)m .. wm-1, takes its values and gates from x_prev / gate_prev, the later half,

@@ -12,7 +12,7 @@ from typing import Optional
 
 from . import _lib
 
-__all__ = ["csa_compress", "compressor_cache_update", "csa_index_topk",
+__all__ = ["csa_compress", "compressor_cache_update", "compressor_cache_update_pair", "csa_index_topk",
            "csa_index_topk_workspace_size", "csa_index_topk_noalloc", "NOALLOC_SCRATCH_BYTES", "swa_concat", "csa_attend", "hca_attend", "hca_attend_pairs",
            "attend_workspace_size", "grouped_out_proj", "linear_bt", "linear_bt_multi", "input_projections", "attention_mask_dump",
            "abi_version", "DSV4Error", "lib"]
@@ -212,6 +212,25 @@ def hca_attend_pairs(q, kv_win, kv_pos0, pool, n_pool, m_hca: int, sink, q_pos0,
         _ptr(q), _ptr(kv_win), _ptr(kv_pos0), kv_win.shape[1], _ptr(pool), N_cap, _ptr(n_pool),
         m_hca, _ptr(sink), _ptr(q_pos0), _ptr(out), B, T, H, D, window, rope_dim,
         float(rope_theta), int(rope_pos_offset), float(scale), _dtype(q), _stream(stream)))
+
+
+def compressor_cache_update_pair(first, second, lengths, m: int, overlap: bool, rope_theta: float = 10000.0,
+                                 rope_pos_offset: int = 0, emit: bool = True, stream=None) -> None:
+    """Two compressor cache updates in one launch.  first / second: dicts with x_new, gate_new
+    [B,C]; x_ring, gate_ring [B,span,C]; bias [span,C] fp32 or None; pool [B,N_cap,C]; rope_dim.
+    Both share lengths [B] int32, m, overlap and N_cap (pool.shape[1])."""
+    B, C = first["x_new"].shape
+    C2 = second["x_new"].shape[1]
+    N_cap = first["pool"].shape[1]
+    if second["pool"].shape[1] != N_cap:
+        raise ValueError("both pools must hold N_cap entries")
+    _check("compressor_cache_update_pair", lib().compressor_cache_update_pair(
+        _ptr(first["x_new"]), _ptr(first["gate_new"]), _ptr(first["x_ring"]), _ptr(first["gate_ring"]),
+        _ptr(first.get("bias")), _ptr(first["pool"]), C, int(first.get("rope_dim", 0)),
+        _ptr(second["x_new"]), _ptr(second["gate_new"]), _ptr(second["x_ring"]), _ptr(second["gate_ring"]),
+        _ptr(second.get("bias")), _ptr(second["pool"]), C2, int(second.get("rope_dim", 0)),
+        _ptr(lengths), B, m, int(bool(overlap)), N_cap, float(rope_theta), int(rope_pos_offset),
+        int(bool(emit)), _dtype(first["x_new"]), _stream(stream)))
 
 
 def grouped_out_proj(attn, w_a, w_b, mid, out, stream=None) -> None:

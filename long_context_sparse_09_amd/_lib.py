@@ -23,6 +23,10 @@ SIGNATURES = {
     "compressor_cache_update": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_double,
                                  c_ll, c_int, c_int, c_void_p], c_int),
+    "compressor_cache_update_pair": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                      c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_double, c_ll,
+                                      c_int, c_int, c_void_p], c_int),
     "grouped_out_proj": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                           c_int, c_int, c_int, c_int, c_void_p], c_int),
     "linear_bt": ([c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p], c_int),

@@ -23,7 +23,7 @@ from typing import Dict
 import numpy as np
 import torch
 
-from . import (attend_workspace_size, compressor_cache_update, csa_attend, csa_compress,
+from . import (attend_workspace_size, compressor_cache_update, compressor_cache_update_pair, csa_attend, csa_compress,
                csa_index_topk, csa_index_topk_workspace_size, hca_attend, swa_concat)
 from .layers import LayerShape
 
@@ -161,12 +161,13 @@ class DecodeCache:
         win = self.win[self.cur]
         flat = lambda t: t.reshape(t.shape[0], t.shape[-1])
         if self.kind == "csa":
-            compressor_cache_update(flat(tok["kv"]), flat(tok["gate"]), self.ring["kv"],
-                                    self.ring["gate"], p["bias"], self.pool, self.lengths_d, sh.m,
-                                    True, sh.r, sh.base)
-            compressor_cache_update(flat(tok["k_idx"]), flat(tok["g_idx"]), self.ring["k_idx"],
-                                    self.ring["g_idx"], p["bias_idx"], self.k_pool,
-                                    self.lengths_d, sh.m, True, 0)
+            # the K=V compressor and the indexer's, one launch
+            compressor_cache_update_pair(
+                {"x_new": flat(tok["kv"]), "gate_new": flat(tok["gate"]), "x_ring": self.ring["kv"],
+                 "gate_ring": self.ring["gate"], "bias": p["bias"], "pool": self.pool, "rope_dim": sh.r},
+                {"x_new": flat(tok["k_idx"]), "gate_new": flat(tok["g_idx"]), "x_ring": self.ring["k_idx"],
+                 "gate_ring": self.ring["g_idx"], "bias": p["bias_idx"], "pool": self.k_pool, "rope_dim": 0},
+                self.lengths_d, sh.m, True, sh.base)
         elif self.kind == "hca":
             compressor_cache_update(flat(tok["kv"]), flat(tok["gate"]), self.ring["kv"],
                                     self.ring["gate"], p["bias_hca"], self.pool, self.lengths_d,

@@ -104,9 +104,11 @@ int compress_common(const void* x, const void* gate, const void* x_prev, const v
                   name);
 }
 
-int cache_update_common(const dsv4::CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int rope_dim,
-                        double rope_theta, long long rope_pos_offset, int emit, int dtype, void* stream,
-                        const char* name) {
+// Argument checks of one compressor cache update; DSV4_OK (0) when it may launch.  *empty is
+// set when there is nothing to do (B == 0).
+int cache_update_check(const dsv4::CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int rope_dim,
+                       double rope_theta, int emit, int dtype, bool* empty) {
+  *empty = false;
   REQUIRE(dtype_ok(dtype), "dtype %d", dtype);
   REQUIRE(B >= 0 && N_cap >= 0, "negative size");
   REQUIRE(m >= 1, "m must be >= 1");
@@ -116,13 +118,25 @@ int cache_update_common(const dsv4::CacheUpdate& u, int B, int C, int m, int ove
     return fail(DSV4_ERR_UNSUPPORTED, "C=%d: need C <= 2048 (multiple of 8) or <= 512", C);
   if ((overlap ? 2 * m : m) > 4096) return fail(DSV4_ERR_UNSUPPORTED, "window span above 4096");
   if (int rc = check_rope(rope_dim, C, rope_theta)) return rc;
-  if (B == 0) return ok();
+  if (B == 0) {
+    *empty = true;
+    return ok();
+  }
   REQUIRE(u.x_new && u.g_new && u.x_ring && u.g_ring && u.lengths, "null required pointer");
   REQUIRE(!emit || u.pool, "pool required when emitting entries");
   for (const void* p : {u.x_new, u.g_new, static_cast<const void*>(u.x_ring), static_cast<const void*>(u.g_ring),
                         u.xp_new, u.gp_new, static_cast<const void*>(u.xp_ring), static_cast<const void*>(u.gp_ring),
                         static_cast<const void*>(u.pool), static_cast<const void*>(u.bias)})
     REQUIRE(!p || aligned16(p), "pointers must be 16-byte aligned");
+  return ok();
+}
+
+int cache_update_common(const dsv4::CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int rope_dim,
+                        double rope_theta, long long rope_pos_offset, int emit, int dtype, void* stream,
+                        const char* name) {
+  bool empty = false;
+  if (int rc = cache_update_check(u, B, C, m, overlap, N_cap, rope_dim, rope_theta, emit, dtype, &empty)) return rc;
+  if (empty) return ok();
   return launched(dsv4::launch_cache_update(u, B, C, m, overlap, N_cap, rope_dim, rope_theta, rope_pos_offset, emit,
                                             dtype, static_cast<hipStream_t>(stream)),
                   name);
@@ -158,6 +172,26 @@ int compressor_cache_update(const void* x_new, const void* gate_new, void* x_rin
                             lengths};
   return cache_update_common(u, B, C, m, overlap, N_cap, rope_dim, rope_theta, rope_pos_offset, emit, dtype,
                              stream, "compressor_cache_update");
+}
+
+int compressor_cache_update_pair(const void* x_new, const void* gate_new, void* x_ring, void* gate_ring,
+                                 const float* bias, void* pool, int C, int rope_dim, const void* x2_new,
+                                 const void* gate2_new, void* x2_ring, void* gate2_ring, const float* bias2,
+                                 void* pool2, int C2, int rope_dim2, const int* lengths, int B, int m, int overlap,
+                                 int N_cap, double rope_theta, long long rope_pos_offset, int emit, int dtype,
+                                 void* stream) {
+  const dsv4::CacheUpdate u[2] = {
+      {x_new, gate_new, x_ring, gate_ring, nullptr, nullptr, nullptr, nullptr, bias, pool, lengths},
+      {x2_new, gate2_new, x2_ring, gate2_ring, nullptr, nullptr, nullptr, nullptr, bias2, pool2, lengths}};
+  const int Cs[2] = {C, C2}, rs[2] = {rope_dim, rope_dim2};
+  bool empty = false;
+  for (int i = 0; i < 2; ++i)
+    if (int rc = cache_update_check(u[i], B, Cs[i], m, overlap, N_cap, rs[i], rope_theta, emit, dtype, &empty))
+      return rc;
+  if (empty) return ok();
+  return launched(dsv4::launch_cache_update(u, Cs, rs, 2, B, m, overlap, N_cap, rope_theta, rope_pos_offset, emit,
+                                            dtype, static_cast<hipStream_t>(stream)),
+                  "compressor_cache_update_pair");
 }
 
 int compressor_cache_update_split(const void* x_new, const void* gate_new, const void* x_prev_new,

@@ -578,11 +578,11 @@ hipError_t launch_compress(const void* x, const void* gate, const void* x_prev, 
 // store and the pooling, so it reads back its own write.
 // ---------------------------------------------------------------------------
 template <typename T, int VEC>
-__global__ void __launch_bounds__(256) cache_update_kernel(
+__device__ __forceinline__ void cache_update_body(
     const T* __restrict__ x_new, const T* __restrict__ g_new, T* x_ring, T* g_ring,
     const T* __restrict__ xp_new, const T* __restrict__ gp_new, T* xp_ring, T* gp_ring,
     const float* __restrict__ bias, T* __restrict__ pool, const int* __restrict__ lengths, int C,
-    int m, int overlap, int N_cap, int r, const RopeFreq rf, long long pos_off, int emit) {
+    int m, int overlap, int N_cap, int r, const RopeFreq& rf, long long pos_off, int emit) {
   __shared__ double inv_freq[kMaxRope / 2];
   for (int i = threadIdx.x; i < r / 2; i += blockDim.x) inv_freq[i] = rf.inv[i];
   __syncthreads();
@@ -665,30 +665,69 @@ __global__ void __launch_bounds__(256) cache_update_kernel(
   }
 }
 
+// One launch updates the compressors given (one, or two of one layer that share lengths, m,
+// overlap and N_cap: the CSA K=V compressor and the indexer's); blockIdx.y picks the compressor,
+// blockIdx.x the sequence.
+template <typename T>
+struct CacheLaunch {
+  CacheUpdate u;
+  int C, r;
+  RopeFreq rf;
+};
+
 template <typename T, int VEC>
-static hipError_t cache_update_t(const CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int r,
-                                 double theta, long long off, int emit, hipStream_t st) {
-  const int G = C / VEC;
+__global__ void __launch_bounds__(256) cache_update_kernel(const CacheLaunch<T> p0, const CacheLaunch<T> p1, int m,
+                                                           int overlap, int N_cap, long long pos_off, int emit) {
+  // one call per compressor on the kernel arguments themselves (selecting a reference to
+  // either copied the argument block, rotary table included, into scratch memory)
+  auto run = [&](const CacheLaunch<T>& p) {
+    const CacheUpdate& u = p.u;
+    cache_update_body<T, VEC>(static_cast<const T*>(u.x_new), static_cast<const T*>(u.g_new),
+                              static_cast<T*>(u.x_ring), static_cast<T*>(u.g_ring), static_cast<const T*>(u.xp_new),
+                              static_cast<const T*>(u.gp_new), static_cast<T*>(u.xp_ring),
+                              static_cast<T*>(u.gp_ring), u.bias, static_cast<T*>(u.pool), u.lengths, p.C, m,
+                              overlap, N_cap, p.r, p.rf, pos_off, emit);
+  };
+  if (blockIdx.y == 0) run(p0);
+  else run(p1);
+}
+
+template <typename T, int VEC>
+static hipError_t cache_update_t(const CacheUpdate* u, const int* C, const int* r, int n, int B, int m, int overlap,
+                                 int N_cap, double theta, long long off, int emit, hipStream_t st) {
+  CacheLaunch<T> p[2];
+  int G = 1;
+  for (int i = 0; i < n; ++i) {
+    p[i] = CacheLaunch<T>{u[i], C[i], r[i], make_rope_freq(r[i], theta)};
+    G = C[i] / VEC > G ? C[i] / VEC : G;
+  }
+  if (n == 1) p[1] = p[0];
   const int threads = G >= 256 ? 256 : ((G + 63) / 64) * 64;
-  hipLaunchKernelGGL((cache_update_kernel<T, VEC>), dim3(B), dim3(threads), 0, st,
-                     static_cast<const T*>(u.x_new), static_cast<const T*>(u.g_new), static_cast<T*>(u.x_ring),
-                     static_cast<T*>(u.g_ring), static_cast<const T*>(u.xp_new), static_cast<const T*>(u.gp_new),
-                     static_cast<T*>(u.xp_ring), static_cast<T*>(u.gp_ring), u.bias, static_cast<T*>(u.pool),
-                     u.lengths, C, m, overlap, N_cap, r, make_rope_freq(r, theta), off, emit);
+  hipLaunchKernelGGL((cache_update_kernel<T, VEC>), dim3(B, n), dim3(threads), 0, st, p[0], p[1], m, overlap, N_cap,
+                     off, emit);
   return hipGetLastError();
+}
+
+hipError_t launch_cache_update(const CacheUpdate* us, const int* Cs, const int* rs, int n, int B, int m, int overlap,
+                               int N_cap, double theta, long long off, int emit, int dtype, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  CacheUpdate v[2];
+  bool v8 = true;
+  for (int i = 0; i < n; ++i) {
+    v[i] = us[i];
+    if (!overlap || v[i].xp_ring == nullptr) v[i].xp_new = v[i].gp_new = v[i].xp_ring = v[i].gp_ring = nullptr;
+    v8 = v8 && (Cs[i] % 8 == 0) && (Cs[i] / 8 <= 256);
+  }
+  if (dtype == 1)
+    return v8 ? cache_update_t<bf16_t, 8>(v, Cs, rs, n, B, m, overlap, N_cap, theta, off, emit, st)
+              : cache_update_t<bf16_t, 2>(v, Cs, rs, n, B, m, overlap, N_cap, theta, off, emit, st);
+  return v8 ? cache_update_t<float, 8>(v, Cs, rs, n, B, m, overlap, N_cap, theta, off, emit, st)
+            : cache_update_t<float, 2>(v, Cs, rs, n, B, m, overlap, N_cap, theta, off, emit, st);
 }
 
 hipError_t launch_cache_update(const CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int r,
                                double theta, long long off, int emit, int dtype, hipStream_t st) {
-  if (B == 0) return hipSuccess;
-  CacheUpdate v = u;
-  if (!overlap || v.xp_ring == nullptr) v.xp_new = v.gp_new = v.xp_ring = v.gp_ring = nullptr;
-  const bool v8 = (C % 8 == 0) && (C / 8 <= 256);
-  if (dtype == 1)
-    return v8 ? cache_update_t<bf16_t, 8>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st)
-              : cache_update_t<bf16_t, 2>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st);
-  return v8 ? cache_update_t<float, 8>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st)
-            : cache_update_t<float, 2>(v, B, C, m, overlap, N_cap, r, theta, off, emit, st);
+  return launch_cache_update(&u, &C, &r, 1, B, m, overlap, N_cap, theta, off, emit, dtype, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -34,6 +34,10 @@ struct CacheUpdate {
 };
 hipError_t launch_cache_update(const CacheUpdate& u, int B, int C, int m, int overlap, int N_cap, int r,
                                double theta, long long off, int emit, int dtype, hipStream_t st);
+// n (1 or 2) compressors that share lengths, m, overlap and N_cap, in one launch; compressor i
+// has width Cs[i] and rotary width rs[i].
+hipError_t launch_cache_update(const CacheUpdate* us, const int* Cs, const int* rs, int n, int B, int m, int overlap,
+                               int N_cap, double theta, long long off, int emit, int dtype, hipStream_t st);
 
 hipError_t launch_swa(const void* kv_raw, void* kv_win, const int* kv_pos0, const int* new_pos0,
                       int B, int S_new, int S_cap, int D, int r, double theta, long long off,

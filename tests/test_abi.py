@@ -167,6 +167,20 @@ def test_cache_update_argument_errors(lib):
     assert call() == INVALID and b"null" in lib.dsv4_last_error()
 
 
+
+def test_cache_update_pair_argument_errors(lib):
+    def call(**kw):
+        a = dict(B=2, C=512, C2=128, m=4, ov=1, r=64, r2=0)
+        a.update(kw)
+        return lib.compressor_cache_update_pair(None, None, None, None, None, None, a["C"], a["r"],
+                                                None, None, None, None, None, None, a["C2"], a["r2"],
+                                                None, a["B"], a["m"], a["ov"], 64, 1e4, 0, 1, BF16, None)
+    assert call(B=0) == OK
+    assert call(m=0) == INVALID
+    assert call(C2=3) == INVALID          # the second compressor's width is checked too
+    assert call(r2=256) == INVALID        # rotary width above the second compressor's C
+    assert call() == INVALID              # null pointers
+
 def test_projection_argument_errors(lib):
     def op(**kw):
         a = dict(T=16, H=64, D=512, G=8, rank=1024, hidden=4096, dtype=BF16)
