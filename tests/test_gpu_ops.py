@@ -137,6 +137,48 @@ def test_cache_update_split_halves_decode():
         assert np.all(got[b, n:] == 0.0), "entries beyond the sequence's closed windows"
 
 
+def test_cache_update_pair_matches_two_calls_and_oracle():
+    """The K=V and indexer-key compressors of a CSA layer updated by one launch
+    (compressor_cache_update_pair): token by token, sequences of different lengths, entries
+    closed every m tokens.  Each pool equals the one two separate calls build (bit for bit) and
+    the oracle's pool of the whole history (one bf16 ulp)."""
+    B, C1, C2, m, r = 3, 512, 128, 4, 64
+    S_b = [21, 30, 8]
+    S = max(S_b)
+    print(f"cache update pair B={B} C={C1},{C2} m={m} S={S_b}", flush=True)
+    xs = [normal(n, (B, S, c)) for n, c in (("x1", C1), ("g1", C1), ("x2", C2), ("g2", C2))]
+    b1, b2 = (normal(n, (2 * m, c)).astype(np.float32) for n, c in (("b1", C1), ("b2", C2)))
+    e = [enc(a, "bf16") for a in xs]
+    N_cap = S // m
+
+    def state():
+        rings = [torch.zeros(B, 2 * m, c, dtype=torch.bfloat16, device="cuda") for c in (C1, C1, C2, C2)]
+        pools = [torch.zeros(B, N_cap, c, dtype=torch.bfloat16, device="cuda") for c in (C1, C2)]
+        return rings, pools
+
+    (ra, pa), (rb, pb) = state(), state()
+    for t in range(S):
+        lens = i32([t + 1 if t < S_b[b] else 0 for b in range(B)])
+        tok = [dev(np.ascontiguousarray(a[:, t])) for a in e]
+        L.compressor_cache_update_pair(
+            {"x_new": tok[0], "gate_new": tok[1], "x_ring": ra[0], "gate_ring": ra[1], "bias": dev(b1),
+             "pool": pa[0], "rope_dim": r},
+            {"x_new": tok[2], "gate_new": tok[3], "x_ring": ra[2], "gate_ring": ra[3], "bias": dev(b2),
+             "pool": pa[1], "rope_dim": 0},
+            lens, m, True, 10000.0)
+        L.compressor_cache_update(tok[0], tok[1], rb[0], rb[1], dev(b1), pb[0], lens, m, True, r, 10000.0)
+        L.compressor_cache_update(tok[2], tok[3], rb[2], rb[3], dev(b2), pb[1], lens, m, True, 0)
+    torch.cuda.synchronize()
+    for i, (bias, rd) in enumerate(((b1, r), (b2, 0))):
+        got, two = host(pa[i]), host(pb[i])
+        assert np.array_equal(got, two), f"compressor {i}: one launch differs from two calls"
+        for b in range(B):
+            n = S_b[b] // m
+            x64, g64 = (W.to_f64(a[b:b + 1, :S_b[b]]) for a in e[2 * i:2 * i + 2])
+            ref = oracle.csa_compress(x64, g64, bias.astype(np.float64), m, True, rd, 10000.0, 0)[0]
+            assert_bf16_ulp(got[b, :n], ref, f"compressor {i}, sequence {b}")
+
+
 # ---------------------------------------------------------------------------- swa_concat
 
 @pytest.mark.parametrize("dt,D,r", [("fp32", 64, 16), ("bf16", 512, 64), ("bf16", 512, 0)])
